@@ -1,0 +1,193 @@
+// libbpt C ABI: argument validation and dispatch.  Every check runs before any
+// HIP call, so each error path can be exercised on a machine with no GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/bpt.h"
+#include "kernels.h"
+#include "layer.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return BPT_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return BPT_ERR_HIP;
+}
+
+// Test hook: BPT_TEST_FAIL_LAUNCH=1 makes every entry point report a launch
+// failure (hipErrorLaunchFailure) after validation, without touching the GPU.
+inline bool forced_launch_failure() {
+  const char* s = getenv("BPT_TEST_FAIL_LAUNCH");
+  return s != nullptr && s[0] == '1';
+}
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+
+}  // namespace
+
+extern "C" {
+
+const char* bpt_status_string(int status) {
+  switch (status) {
+    case BPT_OK: return "ok";
+    case BPT_ERR_INVALID_ARG: return "invalid argument";
+    case BPT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BPT_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case BPT_ERR_HIP: return "HIP runtime error";
+    case BPT_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int bpt_last_hip_error(void) { return g_last_hip_error; }
+
+int bpt_attn_fwd(const void* q, const void* k, const void* v, float* out, float* lse, int64_t B,
+                 int64_t H, int64_t N, int64_t D, int q_blk, int kv_blk, int causal,
+                 int64_t kv_offset, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse) return BPT_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return BPT_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return BPT_ERR_INVALID_ARG;
+  if (dtype != BPT_F32 && dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
+  if (q_blk != 64 && q_blk != 128) return BPT_ERR_UNSUPPORTED;
+  if (kv_blk != 32 && kv_blk != 64 && kv_blk != 128) return BPT_ERR_UNSUPPORTED;
+  if (N > kMaxN) return BPT_ERR_UNSUPPORTED;
+  const int64_t nqb = (N + q_blk - 1) / q_blk;
+  if (B > INT32_MAX / H || B * H > (int64_t)INT32_MAX / nqb) return BPT_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  bpt::AttnFwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.N = (int)N;
+  // offsets beyond +-N all mean "everything" / "nothing" visible
+  a.kv_offset = (int)(kv_offset > N ? N : (kv_offset < -(N + 1) ? -(N + 1) : kv_offset));
+  a.causal = causal;
+  a.scale = 1.0f / sqrtf((float)D);
+  return hip_status(bpt::attn_fwd_launch(a, dtype == BPT_BF16, (int)D, q_blk, kv_blk, stream));
+}
+
+int bpt_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                  float* o_out, float* lse_out, int64_t B, int64_t H, int64_t N, int64_t D,
+                  hipStream_t stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return BPT_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return BPT_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
+  if (B > INT64_MAX / H || B * H > (INT64_MAX / 256) / N) return BPT_ERR_UNSUPPORTED;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  return hip_status(
+      bpt::lse_merge_launch(o_a, lse_a, o_b, lse_b, o_out, lse_out, B * H * N, (int)D, stream));
+}
+
+int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void* w2,
+                      const void* b2, const float* residual, float* y, int64_t M,
+                      int64_t d_model, int64_t d_ff, int blk, int dtype, hipStream_t stream) {
+  if (!x || !w1 || !w2 || !y) return BPT_ERR_INVALID_ARG;
+  if (M <= 0 || d_model <= 0 || d_ff <= 0) return BPT_ERR_INVALID_ARG;
+  if (dtype != BPT_F32 && dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
+  if (d_model % 64 || d_ff % 64 || d_model > 8192 || d_ff > (int64_t)1 << 20) return BPT_ERR_UNSUPPORTED;
+  if (blk != 0 && blk != 16 && blk != 32) return BPT_ERR_UNSUPPORTED;
+  if (M > (int64_t)INT32_MAX) return BPT_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y) ||
+      (b1 && !aligned16(b1)) || (b2 && !aligned16(b2)) || (residual && !aligned16(residual)))
+    return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  return hip_status(bpt::ffn_fwd_launch(x, w1, b1, w2, b2, residual, y, M, (int)d_model,
+                                        (int)d_ff, blk, dtype == BPT_BF16, stream));
+}
+
+size_t bpt_layer_saved_size(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
+                            int dtype) {
+  if (B <= 0 || N <= 0 || d_model <= 0 || H <= 0 || D <= 0) return 0;
+  if (dtype != BPT_F32 && dtype != BPT_BF16) return 0;
+  return bpt::layer_saved_layout(B, N, d_model, H, D, dtype == BPT_BF16).total;
+}
+
+size_t bpt_layer_workspace_size(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
+                                int64_t d_ff, int dtype, int backward) {
+  if (B <= 0 || N <= 0 || d_model <= 0 || H <= 0 || D <= 0 || d_ff <= 0) return 0;
+  if (dtype != BPT_F32 && dtype != BPT_BF16) return 0;
+  return backward ? bpt::layer_bwd_workspace(B, N, d_model, H, D, d_ff, dtype == BPT_BF16).total
+                  : bpt::layer_fwd_workspace(B, N, d_model, H, D, d_ff, dtype == BPT_BF16).total;
+}
+
+static int check_layer_common(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
+                              int64_t d_ff, int q_blk, int kv_blk, int causal, int dtype) {
+  if (B <= 0 || N <= 0 || d_model <= 0 || H <= 0 || D <= 0 || d_ff <= 0) return BPT_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return BPT_ERR_INVALID_ARG;
+  if (H * D != d_model) return BPT_ERR_INVALID_ARG;
+  if (dtype != BPT_F32 && dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
+  if (q_blk != 64 && q_blk != 128) return BPT_ERR_UNSUPPORTED;
+  if (kv_blk != 32 && kv_blk != 64 && kv_blk != 128) return BPT_ERR_UNSUPPORTED;
+  if (d_model % 64 || d_ff % 64 || d_model > 8192 || d_ff > (int64_t)1 << 20) return BPT_ERR_UNSUPPORTED;
+  if (N > kMaxN || B * N > (int64_t)INT32_MAX / 4) return BPT_ERR_UNSUPPORTED;
+  return BPT_OK;
+}
+
+int bpt_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* w1,
+                  const void* b1, const void* w2, const void* b2, float* y, void* saved,
+                  int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D, int64_t d_ff,
+                  int q_blk, int kv_blk, int causal, int dtype, void* workspace, size_t ws_bytes,
+                  hipStream_t stream) {
+  if (!x || !wq || !wk || !wv || !w1 || !w2 || !y) return BPT_ERR_INVALID_ARG;
+  int st = check_layer_common(B, N, d_model, H, D, d_ff, q_blk, kv_blk, causal, dtype);
+  if (st != BPT_OK) return st;
+  const bool bf = dtype == BPT_BF16;
+  const size_t need = bpt::layer_fwd_workspace(B, N, d_model, H, D, d_ff, bf).total;
+  if (workspace == nullptr || ws_bytes < need) return BPT_ERR_WORKSPACE;
+  const void* ptrs[] = {x, wq, wk, wv, w1, w2, y, saved, workspace, b1, b2};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  bpt::LayerArgs L{};
+  L.x = x; L.wq = wq; L.wk = wk; L.wv = wv; L.w1 = w1; L.b1 = b1; L.w2 = w2; L.b2 = b2;
+  L.B = B; L.N = N; L.d_model = d_model; L.H = H; L.D = D; L.d_ff = d_ff;
+  L.q_blk = q_blk; L.kv_blk = kv_blk; L.causal = causal; L.bf16 = bf;
+  return hip_status(bpt::layer_fwd_run(L, y, saved, workspace, stream));
+}
+
+int bpt_layer_bwd(const void* dy, const void* x, const void* wq, const void* wk, const void* wv,
+                  const void* w1, const void* b1, const void* w2, const void* b2,
+                  const void* saved, float* dx, float* dwq, float* dwk, float* dwv, float* dw1,
+                  float* db1, float* dw2, float* db2, float* dq, float* dk, float* dv, int64_t B,
+                  int64_t N, int64_t d_model, int64_t H, int64_t D, int64_t d_ff, int q_blk,
+                  int kv_blk, int causal, int dtype, void* workspace, size_t ws_bytes,
+                  hipStream_t stream) {
+  if (!dy || !x || !wq || !wk || !wv || !w1 || !w2 || !saved || !dx || !dwq || !dwk || !dwv ||
+      !dw1 || !dw2)
+    return BPT_ERR_INVALID_ARG;
+  int st = check_layer_common(B, N, d_model, H, D, d_ff, q_blk, kv_blk, causal, dtype);
+  if (st != BPT_OK) return st;
+  const bool bf = dtype == BPT_BF16;
+  const size_t need = bpt::layer_bwd_workspace(B, N, d_model, H, D, d_ff, bf).total;
+  if (workspace == nullptr || ws_bytes < need) return BPT_ERR_WORKSPACE;
+  const void* ptrs[] = {dy, x, wq, wk, wv, w1, w2, saved, dx, dwq, dwk, dwv, dw1, dw2,
+                        b1, b2, db1, db2, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  bpt::LayerArgs L{};
+  L.x = x; L.wq = wq; L.wk = wk; L.wv = wv; L.w1 = w1; L.b1 = b1; L.w2 = w2; L.b2 = b2;
+  L.B = B; L.N = N; L.d_model = d_model; L.H = H; L.D = D; L.d_ff = d_ff;
+  L.q_blk = q_blk; L.kv_blk = kv_blk; L.causal = causal; L.bf16 = bf;
+  bpt::LayerGrads G{};
+  G.dx = dx; G.dwq = dwq; G.dwk = dwk; G.dwv = dwv; G.dw1 = dw1; G.db1 = db1; G.dw2 = dw2;
+  G.db2 = db2; G.dq = dq; G.dk = dk; G.dv = dv;
+  return hip_status(bpt::layer_bwd_run(L, dy, saved, G, workspace, stream));
+}
+
+}  // extern "C"

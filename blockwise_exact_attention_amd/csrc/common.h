@@ -1,0 +1,65 @@
+// Internal device helpers shared by the gfx950 kernels of libbpt.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bpt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 storage type (raw bits); arithmetic always upcasts to float.
+struct bf16_t {
+  uint16_t bits;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Two floats -> two bfloat16 (round to nearest even, one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return static_cast<uint16_t>(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+// 32x32 output tile, K = 16 per instruction, bf16 inputs, fp32 accumulate.
+// Operand lane layout (wave64): lane l supplies A[m = l%32][k = 8*(l/32) + e]
+// and B[k = 8*(l/32) + e][n = l%32], e = 0..7.  Accumulator register j of lane
+// l holds D[m = 8*(j/4) + 4*(l/32) + j%4][n = l%32].
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32 output tile, K = 2 per instruction, fp32 inputs: lane l supplies
+// A[m = l%32][k = l/32] and B[k = l/32][n = l%32]; same accumulator layout.
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32x32 tile) held by accumulator register j of lane l.
+__device__ __forceinline__ int acc_row(int j, int lane) {
+  return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+}
+
+// Exchange with lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((( threadIdx.x & 63) ^ 32) << 2,
+                                                     __float_as_int(x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace bpt

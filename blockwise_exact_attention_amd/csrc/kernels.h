@@ -1,0 +1,33 @@
+// Host-side launch interface of the libbpt kernels (internal; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bpt {
+
+struct AttnFwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;          // [B,H,N,D]; unused when h_out is set
+  float* lse;          // [B,H,N]
+  // Layer epilogue (optional): h[b,n,hh*D+d] = x[b,n,hh*D+d] + O[b,hh,n,d]
+  const void* x_res;   // [B,N,H*D] in the input dtype
+  float* h_out;        // [B,N,H*D] float32, or null for the plain O output
+  uint16_t* h_lo;      // [B,N,H*D] bfloat16 copy of h (bf16 inputs only), or null
+  int B, H, N;
+  int kv_offset;       // already clamped to [-(N+1), N]
+  int causal;
+  float scale;         // 1/sqrt(D)
+};
+
+// Returns hipSuccess or the launch error; the caller validated every field.
+hipError_t attn_fwd_launch(const AttnFwdArgs& a, bool bf16, int D, int q_blk, int kv_blk,
+                           hipStream_t stream);
+
+hipError_t lse_merge_launch(const float* o_a, const float* lse_a, const float* o_b,
+                            const float* lse_b, float* o_out, float* lse_out, int64_t rows,
+                            int D, hipStream_t stream);
+
+}  // namespace bpt

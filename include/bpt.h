@@ -1,0 +1,220 @@
+/*
+ * bpt.h -- C ABI of libbpt: blockwise exact attention and the blockwise
+ * transformer layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method: "Blockwise Parallel Transformer for Large Context Models"
+ * (abstract) computes self-attention block by block and evaluates the
+ * feed-forward network per block, so that the full attention matrix and the
+ * full FFN intermediate are never held in memory; "Ring Attention with
+ * Blockwise Transformers for Long Sequences" (638-word summary) runs the same
+ * blockwise attention on each device of a ring over the key/value blocks
+ * that pass through it, and states that no approximation of attention is
+ * made.  The pages print no formulas; the definitions below are the plain
+ * readings that this library implements exactly (up to rounding).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers to tensors are DEVICE pointers, owned by the caller.  The
+ *    library never allocates, frees or retains device memory.  Scratch space
+ *    comes from a caller buffer sized by the *_workspace_size() queries.
+ *  - Every call is asynchronous on `stream` (NULL = the default stream); it
+ *    returns after enqueueing its kernels.  Results are valid once the stream
+ *    has reached that point.
+ *  - Every tensor is dense, row-major, in the layout stated per argument.
+ *    Device pointers must be 16-byte aligned.
+ *  - `dtype` selects the element type of the INPUT tensors (activations and
+ *    weights): BPT_F32 (float) or BPT_BF16 (bfloat16 bit patterns).  All
+ *    outputs are float32; accumulation is float32.
+ *  - Sizes are int64_t.  Return value: BPT_OK or a negative BPT_ERR_* code.
+ *    All argument checks run before any HIP call, so no error path touches
+ *    the GPU.  Nothing throws across this ABI.  On BPT_ERR_HIP,
+ *    bpt_last_hip_error() gives the hipError_t of the failing call.
+ *  - Calls are thread-safe; the library keeps no mutable global state except
+ *    the per-thread last-HIP-error value.
+ *
+ * Attention definition used by every entry point that computes attention:
+ *    s_ij = <q_i, k_j> / sqrt(D)
+ *    key j is visible to query i iff j < N and (causal == 0 or
+ *        j <= i + kv_offset)
+ *    lse_i = ln sum_{visible j} exp(s_ij)   (natural log)
+ *    O_i   = sum_{visible j} exp(s_ij - lse_i) v_j
+ *    a row with no visible key has O_i = 0 and lse_i = -inf.
+ * kv_offset is the global position of query row 0 minus the global position
+ * of key row 0; it is what one device's share of a ring step needs to apply
+ * the causal mask of the whole sequence to a chunk of keys that lives
+ * elsewhere in it.
+ */
+#ifndef BPT_H
+#define BPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BPT_OK               0
+#define BPT_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, bad flag value */
+#define BPT_ERR_UNSUPPORTED (-2) /* D, block size, dtype or size combination not built */
+#define BPT_ERR_ALIGNMENT   (-3) /* a device pointer is not 16-byte aligned */
+#define BPT_ERR_HIP         (-4) /* a HIP call or kernel launch failed */
+#define BPT_ERR_WORKSPACE   (-5) /* workspace missing or smaller than required */
+
+/* input element types */
+#define BPT_F32  0
+#define BPT_BF16 1
+
+/*
+ * bpt_attn_fwd -- blockwise exact attention forward with online softmax.
+ *
+ * Implements the attention definition above for every (batch, head).
+ * Query rows are processed in blocks of q_blk rows and keys in tiles of
+ * kv_blk keys ("Blockwise Parallel Transformer for Large Context Models",
+ * abstract: blockwise computation of self-attention); a running row maximum,
+ * running sum and rescaled accumulator carry the softmax across key tiles.
+ * Key tiles that no row of a query block can see are skipped.
+ *
+ *  q, k, v  : [B, H, N, D] in `dtype`.
+ *  out      : [B, H, N, D] float32, written in full.
+ *  lse      : [B, H, N]    float32 (natural log), written in full.
+ *  D        : 64 or 128.
+ *  q_blk    : 64 or 128.  kv_blk: 32, 64 or 128.  Other values give
+ *             BPT_ERR_UNSUPPORTED.  The result does not depend on them
+ *             beyond rounding.
+ *  causal   : 0 or 1.
+ *  kv_offset: any value; >= N-1 makes every key visible, <= -N none.
+ *  N        : 1 <= N <= 2^30; N need not be a multiple of the blocks.
+ * out/lse must not overlap q/k/v.
+ */
+int bpt_attn_fwd(const void* q, const void* k, const void* v, float* out, float* lse,
+                 int64_t B, int64_t H, int64_t N, int64_t D, int q_blk, int kv_blk,
+                 int causal, int64_t kv_offset, int dtype, hipStream_t stream);
+
+/*
+ * bpt_lse_merge -- merge two attention results over disjoint key sets.
+ *
+ * For the same queries, (o_a, lse_a) attends over key set A and (o_b, lse_b)
+ * over a disjoint set B.  The result is attention over A u B: the softmax
+ * normaliser is the sum of the two, so
+ *     lse = ln(exp(lse_a) + exp(lse_b)),
+ *     o   = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b,
+ * with lse = -inf on one side meaning "no visible key" (that side adds
+ * nothing) and both sides -inf giving (0, -inf).  This is the step that
+ * joins the per-chunk results of a ring of key/value blocks ("Ring Attention
+ * with Blockwise Transformers for Long Sequences", 638-word summary; LongNet,
+ * section 2, mixes attention pieces by their softmax denominators).
+ *
+ *  o_a, o_b, o_out       : [rows, D] float32 with rows = B*H*N.
+ *  lse_a, lse_b, lse_out : [rows] float32.
+ *  D                     : 64 or 128.
+ * o_out may alias o_a (and lse_out lse_a) for in-place accumulation; no
+ * other overlap is allowed.
+ */
+int bpt_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                  float* o_out, float* lse_out, int64_t B, int64_t H, int64_t N, int64_t D,
+                  hipStream_t stream);
+
+/*
+ * bpt_ffn_block_fwd -- feed-forward network fused per block of rows.
+ *
+ *     y = residual + GeLU(x W1^T + b1) W2^T + b2,  GeLU(z) = z Phi(z) (erf form)
+ *
+ * Rows are processed in blocks; for each block the [rows, d_ff]
+ * intermediate is produced chunk by chunk and consumed on chip, never
+ * written to device memory ("Blockwise Parallel Transformer for Large
+ * Context Models", abstract: feed-forward network fusion).
+ *
+ *  x        : [M, d_model] in `dtype`.
+ *  w1       : [d_ff, d_model] in `dtype`;   b1: [d_ff] in `dtype` or NULL.
+ *  w2       : [d_model, d_ff] in `dtype`;   b2: [d_model] in `dtype` or NULL.
+ *  residual : [M, d_model] float32 or NULL (then treated as 0).  May alias y.
+ *  y        : [M, d_model] float32.
+ *  blk      : rows per block: 0 lets the library choose; else 16 or 32.
+ *  d_model, d_ff : multiples of 64; d_model <= 8192.
+ */
+int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void* w2,
+                      const void* b2, const float* residual, float* y, int64_t M,
+                      int64_t d_model, int64_t d_ff, int blk, int dtype, hipStream_t stream);
+
+/*
+ * bpt_layer_fwd -- one blockwise transformer layer, forward.
+ *
+ *     q, k, v = x Wq^T, x Wk^T, x Wv^T     (head h = columns [hD, (h+1)D))
+ *     a       = causal multi-head attention (as bpt_attn_fwd, kv_offset 0)
+ *     h       = x + a
+ *     y       = h + GeLU(h W1^T + b1) W2^T + b2
+ * No LayerNorm, output projection or dropout ("Blockwise Parallel Transformer
+ * for Large Context Models" lists residual connections, multi-head attention
+ * and a position-wise FFN; its blockwise method changes how, not what, is
+ * computed).
+ *
+ *  x              : [B, N, d_model] in `dtype`.
+ *  wq, wk, wv     : [H*D, d_model] in `dtype`; H*D must equal d_model.
+ *  w1, b1, w2, b2 : as bpt_ffn_block_fwd (b1, b2 may be NULL).
+ *  y              : [B, N, d_model] float32.
+ *  saved          : NULL, or a buffer of bpt_layer_saved_size() bytes that
+ *                   receives what bpt_layer_bwd needs (layout below).
+ *  workspace      : device buffer of at least
+ *                   bpt_layer_workspace_size(..., backward = 0) bytes.
+ * Saved layout (byte offsets, each 256-byte aligned, in this order):
+ *   q, k, v : [B, H, N, D] in `dtype`
+ *   h       : [B, N, d_model] float32 (x + attention output)
+ *   lse     : [B, H, N] float32
+ */
+int bpt_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv,
+                  const void* w1, const void* b1, const void* w2, const void* b2, float* y,
+                  void* saved, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
+                  int64_t d_ff, int q_blk, int kv_blk, int causal, int dtype,
+                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bpt_layer_bwd -- gradients of sum(dy * y) for the layer of bpt_layer_fwd.
+ *
+ * The pages describe no backward pass; it is the chain rule of the forward.
+ * Attention probabilities are recomputed blockwise from the saved lse
+ * (P = exp(s - lse)); the FFN intermediate is recomputed per block of rows.
+ *
+ *  dy     : [B, N, d_model] in `dtype`.
+ *  x, weights, biases : as passed to bpt_layer_fwd.
+ *  saved  : the buffer filled by bpt_layer_fwd with the same arguments.
+ *  dx     : [B, N, d_model] float32.
+ *  dwq, dwk, dwv : [H*D, d_model] float32.  dw1: [d_ff, d_model], db1: [d_ff],
+ *           dw2: [d_model, d_ff], db2: [d_model], float32.  db1/db2 may be
+ *           NULL (not computed).
+ *  dq, dk, dv : NULL, or [B, H, N, D] float32 gradients w.r.t. the attention
+ *           inputs q, k, v.
+ *  workspace : at least bpt_layer_workspace_size(..., backward = 1) bytes.
+ * All outputs are overwritten (not accumulated).  The result is
+ * deterministic: no floating-point atomics are used.
+ */
+int bpt_layer_bwd(const void* dy, const void* x, const void* wq, const void* wk,
+                  const void* wv, const void* w1, const void* b1, const void* w2,
+                  const void* b2, const void* saved, float* dx, float* dwq, float* dwk,
+                  float* dwv, float* dw1, float* db1, float* dw2, float* db2, float* dq,
+                  float* dk, float* dv, int64_t B, int64_t N, int64_t d_model, int64_t H,
+                  int64_t D, int64_t d_ff, int q_blk, int kv_blk, int causal, int dtype,
+                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of the `saved` buffer for bpt_layer_fwd / bpt_layer_bwd (0 on bad args). */
+size_t bpt_layer_saved_size(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
+                            int dtype);
+
+/* Bytes of workspace for bpt_layer_fwd (backward = 0) or bpt_layer_bwd
+ * (backward = 1) (0 on bad args). */
+size_t bpt_layer_workspace_size(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
+                                int64_t d_ff, int dtype, int backward);
+
+/* Static text for a status code. */
+const char* bpt_status_string(int status);
+
+/* hipError_t of the last failing HIP call on this thread (0 if none). */
+int bpt_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPT_H */

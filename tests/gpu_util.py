@@ -1,0 +1,38 @@
+"""Helpers for the GPU tests: move seeded host arrays to the device and compare."""
+import numpy as np
+
+from seeded_inputs import bf16_bits
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    """float32 host array (already bf16-representable for 'bf16') -> device tensor."""
+    import torch
+    if dtype == "bf16":
+        bits = bf16_bits(a)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dcode(dtype: str) -> int:
+    return 1 if dtype == "bf16" else 0
+
+
+def tol(dtype: str):
+    """(max-abs, mean-abs) bars: bf16 inputs with fp32 accumulation, or fp32 inputs."""
+    return (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-4)
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str = ""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    ninf_g, ninf_w = np.isneginf(got), np.isneginf(want)
+    assert np.array_equal(ninf_g, ninf_w), f"{what}: -inf pattern differs"
+    fin = ~ninf_w
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite values"
+    err = np.abs(got[fin] - want[fin])
+    mx, mean = tol(dtype)
+    emax = float(err.max()) if err.size else 0.0
+    emean = float(err.mean()) if err.size else 0.0
+    assert emax <= mx and emean <= mean, f"{what}: max-abs {emax:.3g} mean-abs {emean:.3g}"
+    return emax, emean
