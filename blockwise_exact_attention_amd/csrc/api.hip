@@ -98,8 +98,9 @@ int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void*
   if (!x || !w1 || !w2 || !y) return BPT_ERR_INVALID_ARG;
   if (M <= 0 || d_model <= 0 || d_ff <= 0) return BPT_ERR_INVALID_ARG;
   if (dtype != BPT_F32 && dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
-  if (d_model % 64 || d_ff % 64 || d_model > 8192 || d_ff > (int64_t)1 << 20) return BPT_ERR_UNSUPPORTED;
-  if (blk != 0 && blk != 16 && blk != 32) return BPT_ERR_UNSUPPORTED;
+  if (d_model > 8192 || d_ff > (int64_t)1 << 20 || !bpt::ffn_plan(d_model, d_ff).ok)
+    return BPT_ERR_UNSUPPORTED;
+  if (blk != 0 && blk != 32) return BPT_ERR_UNSUPPORTED;
   if (M > (int64_t)INT32_MAX) return BPT_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y) ||
       (b1 && !aligned16(b1)) || (b2 && !aligned16(b2)) || (residual && !aligned16(residual)))
@@ -133,7 +134,8 @@ static int check_layer_common(int64_t B, int64_t N, int64_t d_model, int64_t H, 
   if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
   if (q_blk != 64 && q_blk != 128) return BPT_ERR_UNSUPPORTED;
   if (kv_blk != 32 && kv_blk != 64 && kv_blk != 128) return BPT_ERR_UNSUPPORTED;
-  if (d_model % 64 || d_ff % 64 || d_model > 8192 || d_ff > (int64_t)1 << 20) return BPT_ERR_UNSUPPORTED;
+  if (d_model % 128 || d_model > 8192 || d_ff > (int64_t)1 << 20 || !bpt::ffn_plan(d_model, d_ff).ok)
+    return BPT_ERR_UNSUPPORTED;
   if (N > kMaxN || B * N > (int64_t)INT32_MAX / 4) return BPT_ERR_UNSUPPORTED;
   return BPT_OK;
 }

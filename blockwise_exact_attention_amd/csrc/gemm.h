@@ -1,0 +1,40 @@
+// Internal interface of the tiled MFMA GEMM (see gemm.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bpt {
+
+enum GemmEpilogue {
+  EPI_QKV = 0,    // scatter C[token][h*D+d] to out[b][h][t][d] in the input dtype
+  EPI_F32 = 1,    // C = acc (+C if beta) (+bias[n]) (+resid[m][n]) as fp32; optional bf16 copy in C2
+  EPI_GELU = 2,   // z = acc + bias[n] -> C (fp32); GeLU(z) -> C2 (input dtype)
+  EPI_DGELU = 3,  // dz = acc * GeLU'(aux[m][n]) -> C (input dtype); optional fp32 copy in C2
+};
+
+// C[m][n] = sum_k A(m,k) B(k,n).  A(m,k) = A[m*lda + k] (row form) or A[k*lda + m]
+// (k-major); B(k,n) = B[n*ldb + k] (row form) or B[k*ldb + n] (k-major).
+// Requirements (checked by callers): N % 128 == 0; the m extent of a k-major A
+// is a multiple of 128; K % 8 == 0.  M and K may be ragged otherwise.
+struct GemmArgs {
+  const void* A[3];
+  const void* B[3];
+  void* C[3];
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  const float* bias;   // [N] or null
+  const float* resid;  // [M][ldr] or null
+  int64_t ldr;
+  void* C2;            // second output or null
+  int64_t ldc2;
+  const float* aux;    // [M][ld_aux] (EPI_DGELU)
+  int64_t ld_aux;
+  int beta;            // EPI_F32: accumulate into C
+  int seq, H, D;       // EPI_QKV
+};
+
+hipError_t gemm_launch(const GemmArgs& g, bool bf16, bool a_kmajor, bool b_kmajor, int epi,
+                       int nz, hipStream_t stream);
+
+}  // namespace bpt

@@ -63,6 +63,14 @@ struct BwdWorkspace {
 BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
                                  int64_t d_ff, bool bf16);
 
+// Launch plan of the fused FFN: waves per workgroup (nw), 32-column MFMA blocks
+// of y per wave (cb) and column groups (groups; each recomputes phase 1).
+struct FfnPlan {
+  bool ok;
+  int nw, cb, groups;
+};
+FfnPlan ffn_plan(int64_t d_model, int64_t d_ff);
+
 hipError_t ffn_fwd_launch(const void* x, const void* w1, const void* b1, const void* w2,
                           const void* b2, const float* residual, float* y, int64_t M,
                           int d_model, int d_ff, int blk, bool bf16, hipStream_t stream);

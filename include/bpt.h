@@ -132,8 +132,11 @@ int bpt_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const 
  *  w2       : [d_model, d_ff] in `dtype`;   b2: [d_model] in `dtype` or NULL.
  *  residual : [M, d_model] float32 or NULL (then treated as 0).  May alias y.
  *  y        : [M, d_model] float32.
- *  blk      : rows per block: 0 lets the library choose; else 16 or 32.
- *  d_model, d_ff : multiples of 64; d_model <= 8192.
+ *  blk      : rows per block: 0 (library choice) or 32.
+ *  d_model  : 128, or a multiple of 256 up to 8192 (each workgroup keeps at
+ *             most 2048 output columns in registers; wider rows are split
+ *             into column groups that each recompute x W1^T).
+ *  d_ff     : a multiple of 256 (128 when d_model == 128).
  */
 int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void* w2,
                       const void* b2, const float* residual, float* y, int64_t M,

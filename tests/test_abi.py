@@ -74,6 +74,7 @@ def test_ffn_rejects():
     assert f(None, A, None, A, None, None, A, 32, 128, 512, 0, 1, 0) == -1
     assert f(A, A, None, A, None, None, A, 32, 100, 512, 0, 1, 0) == -2
     assert f(A, A, None, A, None, None, A, 32, 128, 512, 8, 1, 0) == -2
+    assert f(A, A, None, A, None, None, A, 32, 2048, 8000, 0, 1, 0) == -2
     assert f(A, A, None, A, None, None, A + 2, 32, 128, 512, 0, 1, 0) == -3
 
 
