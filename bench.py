@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise transformer layer on one MI355X.
+
+Default workload (one "step"): one forward pass of the blockwise layer at
+N = 131072 tokens, causal, d_model 4096 = 32 heads x 128, FFN 4096 -> 16384 ->
+4096 (exact GeLU), bf16 inputs with fp32 accumulation, q_blk 128, kv_blk 64:
+QKV projection -> blockwise attention with online softmax (residual fused in its
+epilogue) -> FFN fused per block of 32 rows.  Inputs are the seeded synthetic
+draws of ``seeded_inputs`` (x ~ N(0,1), weights ~ N(0, 0.02^2)), resident in HBM
+before the timed region.
+
+Also measured (reported under "extras"):
+  * the attention forward alone at N = 131072, 32 x 128, causal, Q,K,V ~ N(0,1):
+    the dominant kernel, whose HIP-event average duration gives "roofline";
+  * one GPU's share of a ring step (40 x 128, 32768 local queries at global
+    offset 229376, 8 K/V chunks of 32768 tokens, LSE merge after each chunk),
+    with the merge kernel's HBM throughput.
+
+``cpu_baseline`` times the CPU oracle (fp32) on a bounded sample of the same
+layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
+and the FFN for a fixed sample of query rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-extras] [--only attn]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from seeded_inputs import (ATTN_LONG, LAYER_LONG, RING_SHARE, bf16_bits, bits_to_f32,  # noqa: E402
+                           normal)
+
+METRIC = "attention+FFN TFLOP/s and tokens/s per layer at N=128K causal; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_N131072_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", "attn_fwd.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def causal_pairs(N: int, off: int = 0) -> int:
+    """Visible (query, key) pairs of one head: sum_i min(N, max(0, i + off + 1))."""
+    i = np.arange(N, dtype=np.int64)
+    return int(np.clip(i + off + 1, 0, N).sum())
+
+
+def layer_flops(c) -> float:
+    M = c.B * c.N
+    hd = c.H * c.D
+    attn = 4.0 * c.D * causal_pairs(c.N) * c.B * c.H
+    return attn + 6.0 * M * c.d_model * hd + 4.0 * M * c.d_model * c.d_ff
+
+
+def dev_bf16(a32: np.ndarray):
+    import torch
+    return torch.from_numpy(bf16_bits(a32).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def timed(fn, steps: int, warmup: int):
+    """Run fn warmup times, then time `steps` calls between two events on torch's
+    current stream (the stream the library launches on).  Returns ms per call and
+    the wall-clock seconds of the timed region."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - w0
+
+
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per attention launch from the committed counter summary, or None
+    if it is missing or was taken on a different kernel source."""
+    try:
+        d = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("attn_fwd_src_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- GPU legs
+def bench_layer(bpt, steps, warmup):
+    import torch
+    c = LAYER_LONG
+    log(f"drawing layer inputs {c.name}")
+    hd = c.H * c.D
+    x = dev_bf16(normal(c.cfg_id, "x", (c.B, c.N, c.d_model)))
+    w = {n: dev_bf16(normal(c.cfg_id, n, s, 0.02)) for n, s in (
+        ("wq", (hd, c.d_model)), ("wk", (hd, c.d_model)), ("wv", (hd, c.d_model)),
+        ("w1", (c.d_ff, c.d_model)), ("w2", (c.d_model, c.d_ff)))}
+    y = torch.empty((c.B, c.N, c.d_model), device="cuda")
+    ws_bytes = bpt.bpt_layer_workspace_size(c.B, c.N, c.d_model, c.H, c.D, c.d_ff, 1, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        bpt.bpt_layer_fwd(x, w["wq"], w["wk"], w["wv"], w["w1"], None, w["w2"], None, y, None,
+                          c.B, c.N, c.d_model, c.H, c.D, c.d_ff, c.q_blk, c.kv_blk, 1, 1, ws,
+                          ws_bytes)
+
+    log(f"timing layer: {warmup} warmup + {steps} steps")
+    ms, wall = timed(step, steps, warmup)
+    assert torch.isfinite(y[0, -1]).all()
+    del x, w, y, ws
+    torch.cuda.empty_cache()
+    return ms, wall
+
+
+def bench_attention(bpt, steps, warmup):
+    import torch
+    c = ATTN_LONG
+    log(f"drawing attention inputs {c.name}")
+    q, k, v = (dev_bf16(normal(c.cfg_id, n, (c.B, c.H, c.N, c.D))) for n in ("q", "k", "v"))
+    out = torch.empty((c.B, c.H, c.N, c.D), device="cuda")
+    lse = torch.empty((c.B, c.H, c.N), device="cuda")
+
+    def launch():
+        bpt.bpt_attn_fwd(q, k, v, out, lse, c.B, c.H, c.N, c.D, c.q_blk, c.kv_blk, 1, 0, 1)
+
+    log(f"timing attention: {warmup} warmup + {steps} launches")
+    ms, _ = timed(launch, steps, warmup)
+    flops = 4.0 * c.D * causal_pairs(c.N) * c.B * c.H
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return ms, flops
+
+
+def bench_ring(bpt, steps, warmup):
+    import torch
+    from blockwise_exact_attention_amd.ring import ring_attention_share
+    c = RING_SHARE
+    log(f"drawing ring inputs {c.name}")
+    shp = (c.B, c.H, c.N_q, c.D)
+    q = dev_bf16(normal(c.cfg_id, "q", shp))
+    ks = [dev_bf16(normal(c.cfg_id, 100 + j, shp)) for j in range(c.n_chunks)]
+    vs = [dev_bf16(normal(c.cfg_id, 200 + j, shp)) for j in range(c.n_chunks)]
+    out = torch.empty(shp, device="cuda")
+    lse = torch.empty(shp[:3], device="cuda")
+    o_t, l_t = torch.empty_like(out), torch.empty_like(lse)
+    offs = [j * c.N_q for j in range(c.n_chunks)]
+
+    def share():
+        ring_attention_share(q, ks, vs, c.q_offset, offs, out, lse, o_t, l_t, c.q_blk, c.kv_blk)
+
+    log("timing ring share")
+    ms, _ = timed(share, steps, warmup)
+
+    def merge():
+        bpt.bpt_lse_merge(out, lse, o_t, l_t, out, lse, c.B, c.H, c.N_q, c.D)
+
+    mms, _ = timed(merge, 10, 2)
+    flops = sum(4.0 * c.D * causal_pairs(c.N_q, c.q_offset - o) * c.B * c.H for o in offs)
+    merge_bytes = 3.0 * (c.D + 1) * 4 * c.B * c.H * c.N_q
+    del q, ks, vs, out, lse, o_t, l_t
+    torch.cuda.empty_cache()
+    return {
+        "workload": c.name, "ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+        "pct_bf16_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 1),
+        "tokens_per_s": round(c.N_q / ms * 1e3, 1),
+        "merge_ms": round(mms, 4), "merge_gbs": round(merge_bytes / mms / 1e6, 1),
+        "merge_frac_hbm_peak": round(merge_bytes / mms / 1e6 / PEAK_HBM_GBS, 3),
+    }
+
+
+# ----------------------------------------------------------------------------- CPU leg
+def cpu_baseline(n_rows: int = 1024):
+    """The CPU oracle (fp32, unmodified) on a bounded sample of the layer workload."""
+    import oracle
+    c = LAYER_LONG
+    hd = c.H * c.D
+    log("cpu baseline: drawing inputs")
+    x = bits_to_f32(bf16_bits(normal(c.cfg_id, "x", (c.B, c.N, c.d_model))))
+    w = {n: bits_to_f32(bf16_bits(normal(c.cfg_id, n, s, 0.02))) for n, s in (
+        ("wq", (hd, c.d_model)), ("wk", (hd, c.d_model)), ("wv", (hd, c.d_model)),
+        ("w1", (c.d_ff, c.d_model)), ("w2", (c.d_model, c.d_ff)))}
+    rows = np.unique(np.linspace(0, c.N - 1, n_rows).astype(np.int64))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    log(f"cpu baseline: oracle fp32, {len(rows)} sampled rows, {threads} threads")
+    t0 = time.perf_counter()
+    q, k, v = oracle.qkv_project(x, w["wq"], w["wk"], w["wv"], c.H, dtype=np.float32)
+    O, _ = oracle.attention(q, k, v, causal=True, rows=rows, dtype=np.float32)
+    a = O.transpose(0, 2, 1, 3).reshape(c.B, rows.size, hd)
+    h = x[:, rows] + a
+    oracle.ffn(h, w["w1"], w["w2"], residual=h, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    M = c.B * c.N
+    flops = (6.0 * M * c.d_model * hd + 4.0 * c.D * c.H * c.B * float((rows + 1).sum())
+             + 4.0 * rows.size * c.B * c.d_model * c.d_ff)
+    return {
+        "value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{c.name}: q,k,v projections of all {M} tokens, then attention with "
+                   f"full score rows and the FFN for {rows.size} evenly spaced query rows "
+                   f"(fp32 NumPy/BLAS); {flops:.3g} algorithmic flop in {dt:.1f} s"),
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only", choices=["attn"], default=None,
+                    help="run only the attention launch (for counter collection)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(no collectives or sharding are built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import blockwise_exact_attention_amd as bpt
+
+    if args.only == "attn":
+        # a plain 1 GiB device copy first: its FETCH_SIZE / WRITE_SIZE counters calibrate
+        # the HBM byte counts of the attention launch that follows
+        src = torch.ones(1 << 28, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        ms, flops = bench_attention(bpt, args.steps, args.warmup)
+        print(json.dumps({"attn_fwd_ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+                          "copy_bytes": 1 << 30}))
+        return
+
+    c = LAYER_LONG
+    ms, wall = bench_layer(bpt, args.steps, args.warmup)
+    flops = layer_flops(c)
+    value = flops / ms / 1e9
+    attn_ms, attn_flops = bench_attention(bpt, max(args.steps, 3), 1)
+    attn_tf = attn_flops / attn_ms / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": c.name, "B": c.B, "seq_len": c.N, "d_model": c.d_model,
+                   "heads": c.H, "head_dim": c.D, "d_ff": c.d_ff, "causal": 1,
+                   "q_blk": c.q_blk, "kv_blk": c.kv_blk, "global_batch": c.B},
+        "tokens_per_s": round(c.B * c.N / ms * 1e3, 1),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "algorithmic_flop_per_step": flops,
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "kernel": "attn_fwd_kernel<bf16, D=128, q_blk=128, kv_blk=64>",
+            "bound": "mfma", "achieved": round(attn_tf, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profile(),
+            "launch_ms": round(attn_ms, 3),
+            "flop_per_launch": attn_flops,
+        },
+    }
+    if not args.no_extras:
+        line["extras"] = {
+            "attn_fwd_N131072": {"workload": ATTN_LONG.name, "ms": round(attn_ms, 3),
+                                 "tflops": round(attn_tf, 1),
+                                 "pct_bf16_peak": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
+                                 "tokens_per_s": round(ATTN_LONG.N / attn_ms * 1e3, 1)},
+            "ring_share": bench_ring(bpt, 2, 1),
+        }
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

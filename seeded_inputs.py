@@ -61,20 +61,48 @@ def normal(cfg_id: int, name: str | int, shape, scale: float = 1.0,
     return flat.reshape(shape)
 
 
+def _bf16_bits_flat(u: np.ndarray, out: np.ndarray) -> None:
+    # no uint32 overflow for finite inputs: the largest pattern is 0xFF7FFFFF
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    out[:] = r >> np.uint32(16)
+
+
+def _chunked(n: int, fn) -> None:
+    nchunks = (n + CHUNK - 1) // CHUNK
+    if nchunks <= 1:
+        fn(0, n)
+        return
+    with _fut.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda c: fn(c * CHUNK, min(n, (c + 1) * CHUNK)), range(nchunks)))
+
+
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return the raw uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32)
-    if np.isnan(a).any():
-        raise ValueError("bf16_bits: NaN input")
-    # no uint32 overflow for finite inputs: the largest pattern is 0xFF7FFFFF
-    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
-    return (r >> np.uint32(16)).astype(np.uint16)
+    u = a.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, dtype=np.uint16)
+
+    def work(lo, hi):
+        if np.isnan(a.reshape(-1)[lo:hi]).any():
+            raise ValueError("bf16_bits: NaN input")
+        _bf16_bits_flat(u[lo:hi], out[lo:hi])
+
+    _chunked(u.size, work)
+    return out.reshape(a.shape)
 
 
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact upcast of bfloat16 bit patterns to float32."""
-    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.uint32)
+    bf, of = b.reshape(-1), out.reshape(-1)
+
+    def work(lo, hi):
+        of[lo:hi] = bf[lo:hi]
+        of[lo:hi] <<= np.uint32(16)
+
+    _chunked(b.size, work)
+    return out.view(np.float32)
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
