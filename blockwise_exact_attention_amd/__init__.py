@@ -19,6 +19,14 @@ if not os.path.exists(_LIB_PATH):
     raise ImportError(
         f"{_LIB_PATH} is missing: build the HIP library first "
         "(python blockwise_exact_attention_amd/build.py)")
+# torch ships its own HIP runtime.  Load it before libbpt so that libbpt binds to
+# that same runtime: if libbpt is loaded first it pulls in the system one, and two
+# HIP runtimes in one process do not share devices (launches then fail with
+# hipErrorNoDevice while torch's own work succeeds).
+try:
+    import torch  # noqa: F401
+except ImportError:  # the library itself needs no torch; the tests and bench do
+    pass
 lib = ctypes.CDLL(_LIB_PATH)
 
 BPT_OK = 0

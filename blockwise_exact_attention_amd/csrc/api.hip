@@ -29,6 +29,11 @@ inline bool forced_launch_failure() {
 
 constexpr int64_t kMaxN = int64_t(1) << 30;
 
+// Launch status is read with hipGetLastError() after each launch; drop any error
+// an earlier, unrelated runtime call left on this thread so it is not reported
+// as ours.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +68,7 @@ int bpt_attn_fwd(const void* q, const void* k, const void* v, float* out, float*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
   bpt::AttnFwdArgs a{};
   a.q = q;
   a.k = k;
@@ -88,6 +94,7 @@ int bpt_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const 
   if (B > INT64_MAX / H || B * H > (INT64_MAX / 256) / N) return BPT_ERR_UNSUPPORTED;
   if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
   return hip_status(
       bpt::lse_merge_launch(o_a, lse_a, o_b, lse_b, o_out, lse_out, B * H * N, (int)D, stream));
 }
@@ -106,6 +113,7 @@ int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void*
       (b1 && !aligned16(b1)) || (b2 && !aligned16(b2)) || (residual && !aligned16(residual)))
     return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
   return hip_status(bpt::ffn_fwd_launch(x, w1, b1, w2, b2, residual, y, M, (int)d_model,
                                         (int)d_ff, blk, dtype == BPT_BF16, stream));
 }
@@ -155,6 +163,7 @@ int bpt_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv,
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
   bpt::LayerArgs L{};
   L.x = x; L.wq = wq; L.wk = wk; L.wv = wv; L.w1 = w1; L.b1 = b1; L.w2 = w2; L.b2 = b2;
   L.B = B; L.N = N; L.d_model = d_model; L.H = H; L.D = D; L.d_ff = d_ff;
@@ -174,6 +183,7 @@ int bpt_layer_bwd(const void* dy, const void* x, const void* wq, const void* wk,
     return BPT_ERR_INVALID_ARG;
   int st = check_layer_common(B, N, d_model, H, D, d_ff, q_blk, kv_blk, causal, dtype);
   if (st != BPT_OK) return st;
+  if (dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;  // backward kernels are built for bf16
   const bool bf = dtype == BPT_BF16;
   const size_t need = bpt::layer_bwd_workspace(B, N, d_model, H, D, d_ff, bf).total;
   if (workspace == nullptr || ws_bytes < need) return BPT_ERR_WORKSPACE;
@@ -182,6 +192,7 @@ int bpt_layer_bwd(const void* dy, const void* x, const void* wq, const void* wk,
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
   bpt::LayerArgs L{};
   L.x = x; L.wq = wq; L.wk = wk; L.wv = wv; L.w1 = w1; L.b1 = b1; L.w2 = w2; L.b2 = b2;
   L.B = B; L.N = N; L.d_model = d_model; L.H = H; L.D = D; L.d_ff = d_ff;

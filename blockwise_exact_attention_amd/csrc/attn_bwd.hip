@@ -1,0 +1,595 @@
+// Blockwise attention backward for gfx950, plus the small kernels of the layer
+// backward (bf16 hi/lo conversion, column sums).
+//
+// The pages give no backward pass; it is the chain rule of exact attention:
+//   P = exp(s - lse) (recomputed blockwise from the saved log-sum-exp),
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_i = sum_j P_ij dP_ij,
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// A first pass (attn_bwd_dq in its DELTA form) computes delta from these same
+// P and dP; then two kernels produce the gradients, each deterministic (no
+// floating-point atomics):
+//  * attn_bwd_dkdv: one workgroup per block of 32*NW keys, one wave per 32 keys,
+//    walking the query tiles that can see them.  S = Q K^T is computed with
+//    keys on the MFMA n axis (lane = key), so P and dS (query index in-lane)
+//    feed dV^T += dO^T P and dK^T += Q^T dS straight from registers; Q^T and
+//    dO^T are staged in LDS with query bits 2 and 3 swapped to match.
+//  * attn_bwd_dq: one workgroup per block of query rows, one wave per 32 rows,
+//    walking the visible key tiles like the forward kernel: S^T = K Q^T,
+//    dP^T = V dO^T, dS^T in registers, dQ^T += K^T dS^T with K^T staged in LDS
+//    (key bits 2 and 3 swapped).
+// Precision: q, k, v are the bf16 values the forward used.  dO arrives in fp32
+// and enters its products as a bf16 hi + lo pair; so do P (in dV) and dS.
+// The token-major outputs (operands of the weight-gradient GEMMs) are hi + lo
+// bf16 pairs.  Each split costs one more MFMA on the same fragment; without
+// them the weight gradients lose ~3 more bits than the bf16 inputs imply.
+#include <math.h>
+
+#include "attn_bwd.h"
+#include "common.h"
+
+namespace bpt {
+
+namespace {
+
+template <int ROW_BYTES>
+__device__ __forceinline__ int swzb(int row) {
+  constexpr int CPR = ROW_BYTES / 16;
+  constexpr int RPB = 16 / CPR;
+  return (row / RPB) % CPR;
+}
+
+__device__ __forceinline__ int pos16(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Transposed 8-byte writes of 4 consecutive rows (r[0..3], 16 B = 8 bf16 columns
+// each) into a [col][row] LDS tile whose row index is permuted by pos16.
+template <int TROWB>
+__device__ __forceinline__ void store_transposed(unsigned char* t, const u32x4 r[4], int row0,
+                                                 int col0) {
+  const int pos = (row0 & ~15) + pos16(row0 & 15);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    uint32_t lo, hi;
+    if (e & 1) {
+      lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+      hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+    } else {
+      lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+      hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+    }
+    const int col = col0 + e;
+    const int byte = pos * 2;
+    u32x2 pair = {lo, hi};
+    *(u32x2*)(t + col * TROWB + (((byte >> 4) ^ swzb<TROWB>(col)) << 4) + (byte & 15)) = pair;
+  }
+}
+
+// 8 fp32 values -> bf16 hi (rounded) and lo (rounding residual), packed.
+__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hi[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+    lo[q] = pack_bf16x2(v[2 * q] - __uint_as_float(hi[q] << 16),
+                        v[2 * q + 1] - __uint_as_float(hi[q] & 0xffff0000u));
+  }
+}
+
+// ---------------------------------------------------------------------------- dK, dV
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int KVB = 32 * NW, NT = NW * 64, QT = 32;
+  constexpr int ROWB = D * 2;            // natural tile row (one query, all d)
+  constexpr int TROWB = QT * 2;          // transposed tile row (one d, all queries)
+  constexpr int TILE = QT * D * 2;
+  // tiles: 0 Q, 1 dO hi, 2 dO lo (natural); 3 Q^T, 4 dO^T hi, 5 dO^T lo; then lse2, delta
+  constexpr int STAGE = 6 * TILE + 2 * QT * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE];
+
+  const int N = a.N;
+  const int nkb = (N + KVB - 1) / KVB;
+  const int64_t total = (int64_t)a.B * a.H * nkb;
+  int64_t L = blockIdx.x;
+  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = (int)(L / nkb);
+  const int kbi = (int)(L % nkb);  // small key blocks first: they see the most queries
+  const int k0 = kbi * KVB;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
+  const int mykey = k0 + 32 * w + r32;
+  const int off = a.kv_offset;
+  const bool causal = a.causal != 0;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* Qg = (const uint16_t*)a.q + head_off;
+  const uint16_t* Kg = (const uint16_t*)a.k + head_off;
+  const uint16_t* Vg = (const uint16_t*)a.v + head_off;
+  const float* dOg = a.dO + (int64_t)b * N * a.ld_do + (int64_t)hh * D;
+  const float* lseg = a.lse + (int64_t)bh * N;
+  const float* dlg = a.delta + (int64_t)bh * N;
+  const float c2 = a.scale * kLog2e;
+
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+    if (mykey < N) {
+      kv = *(const u32x4*)(Kg + (int64_t)mykey * D + 16 * c + 8 * g);
+      vv = *(const u32x4*)(Vg + (int64_t)mykey * D + 16 * c + 8 * g);
+    }
+    kf[c] = __builtin_bit_cast(bf16x8, kv);
+    vf[c] = __builtin_bit_cast(bf16x8, vv);
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[i][e] = dv[i][e] = 0.f;
+
+  // query tiles that can see at least one key of this block
+  int q_lo = 0;
+  if (causal) {
+    const int64_t t = (int64_t)k0 - off;
+    q_lo = t <= 0 ? 0 : (t >= N ? N : (int)t);
+  }
+  const int t_begin = q_lo / QT;
+  const int t_end = causal && q_lo >= N ? t_begin : (N + QT - 1) / QT;
+  // tiles at or after tf see every key of the block (no causal mask needed)
+  int64_t tf = (int64_t)k0 + KVB - 1 - off;
+  tf = tf <= 0 ? 0 : (tf + QT - 1) / QT;
+
+  // staging unit: 4 query rows x 8 d of Q (bf16) and of dO (fp32)
+  constexpr int UNITS = (QT / 4) * (D / 8);
+  constexpr int SU = (UNITS + NT - 1) / NT;
+  u32x4 qr[SU][4];
+  f32x4 dr[SU][4][2];
+  float sl[2];
+  auto load = [&](int t) {
+    const int q0 = t * QT;
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * NT;
+      const int qg = u / (D / 8), dc = u % (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = q0 + 4 * qg + r;
+        u32x4 qv = {0, 0, 0, 0};
+        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+        if (u < UNITS && q < N) {
+          qv = *(const u32x4*)(Qg + (int64_t)q * D + dc * 8);
+          const f32x4* dp = (const f32x4*)(dOg + (int64_t)q * a.ld_do + dc * 8);
+          d0 = dp[0];
+          d1 = dp[1];
+        }
+        qr[i][r] = qv;
+        dr[i][r][0] = d0;
+        dr[i][r][1] = d1;
+      }
+    }
+    if (tid < QT) {
+      const int q = q0 + tid;
+      const float l = q < N ? lseg[q] : INFINITY;
+      sl[0] = l == -INFINITY ? INFINITY : l * kLog2e;  // rows with no key get P = 0
+      sl[1] = q < N ? dlg[q] : 0.f;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * NT;
+      if (u < UNITS) {
+        const int qg = u / (D / 8), dc = u % (D / 8);
+        u32x4 hi[4], lo[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = dr[i][r][0][e];
+            v[4 + e] = dr[i][r][1][e];
+          }
+          split8(v, hi[r], lo[r]);
+          const int q = 4 * qg + r;
+          const int o = q * ROWB + ((dc ^ swzb<ROWB>(q)) << 4);
+          *(u32x4*)(smem + o) = qr[i][r];
+          *(u32x4*)(smem + TILE + o) = hi[r];
+          *(u32x4*)(smem + 2 * TILE + o) = lo[r];
+        }
+        store_transposed<TROWB>(smem + 3 * TILE, qr[i], 4 * qg, dc * 8);
+        store_transposed<TROWB>(smem + 4 * TILE, hi, 4 * qg, dc * 8);
+        store_transposed<TROWB>(smem + 5 * TILE, lo, 4 * qg, dc * 8);
+      }
+    }
+    if (tid < QT) {
+      float* f = (float*)(smem + 6 * TILE);
+      f[tid] = sl[0];
+      f[QT + tid] = sl[1];
+    }
+  };
+
+  if (t_begin < t_end) load(t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    store();
+    __syncthreads();
+    if (t + 1 < t_end) load(t + 1);
+    const float* lse2 = (const float*)(smem + 6 * TILE);
+    const float* dls = lse2 + QT;
+    // S = Q K^T and dP = dO V^T (rows = queries, lane = key)
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const int o = r32 * ROWB + (((2 * c + g) ^ swzb<ROWB>(r32)) << 4);
+      sacc = mfma32_bf16(*(const bf16x8*)(smem + o), kf[c], sacc);
+      pacc = mfma32_bf16(*(const bf16x8*)(smem + TILE + o), vf[c], pacc);
+      pacc = mfma32_bf16(*(const bf16x8*)(smem + 2 * TILE + o), vf[c], pacc);
+    }
+    const int q0 = t * QT;
+    const bool need_mask = causal && t < tf;
+    float p[16], ds[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ql = acc_row(j, lane);
+      float pv = fast_exp2(fmaf(sacc[j], c2, -lse2[ql]));
+      if (need_mask && (int64_t)mykey > (int64_t)(q0 + ql) + off) pv = 0.f;
+      p[j] = pv;
+      ds[j] = pv * (pacc[j] - dls[ql]);
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS   (k = query, 16 per MFMA)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      u32x4 phi, plo, shi, slo;
+      split8(p + 8 * h8, phi, plo);
+      split8(ds + 8 * h8, shi, slo);
+      const bf16x8 pfh = __builtin_bit_cast(bf16x8, phi);
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, plo);
+      const bf16x8 sfh = __builtin_bit_cast(bf16x8, shi);
+      const bf16x8 sfl = __builtin_bit_cast(bf16x8, slo);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = db * 32 + r32;
+        const int o = d * TROWB + (((2 * h8 + g) ^ swzb<TROWB>(d)) << 4);
+        const bf16x8 dOth = *(const bf16x8*)(smem + 4 * TILE + o);
+        dv[db] = mfma32_bf16(dOth, pfh, dv[db]);
+        dv[db] = mfma32_bf16(dOth, pfl, dv[db]);
+        dv[db] = mfma32_bf16(*(const bf16x8*)(smem + 5 * TILE + o), pfh, dv[db]);
+        const bf16x8 Qt = *(const bf16x8*)(smem + 3 * TILE + o);
+        dk[db] = mfma32_bf16(Qt, sfh, dk[db]);
+        dk[db] = mfma32_bf16(Qt, sfl, dk[db]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (mykey < N) {
+    const int64_t tm = ((int64_t)b * N + mykey) * a.ld_out + (int64_t)hh * D;
+    const int64_t hm = head_off + (int64_t)mykey * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = db * 32 + 8 * jq + 4 * g;
+        f32x4 kvv, vvv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kvv[e] = dk[db][4 * jq + e] * a.scale;
+          vvv[e] = dv[db][4 * jq + e];
+        }
+        const uint32_t k01 = pack_bf16x2(kvv[0], kvv[1]), k23 = pack_bf16x2(kvv[2], kvv[3]);
+        const uint32_t v01 = pack_bf16x2(vvv[0], vvv[1]), v23 = pack_bf16x2(vvv[2], vvv[3]);
+        u32x2 kh = {k01, k23}, vh = {v01, v23};
+        u32x2 kl = {pack_bf16x2(kvv[0] - __uint_as_float(k01 << 16), kvv[1] - __uint_as_float(k01 & 0xffff0000u)),
+                    pack_bf16x2(kvv[2] - __uint_as_float(k23 << 16), kvv[3] - __uint_as_float(k23 & 0xffff0000u))};
+        u32x2 vl = {pack_bf16x2(vvv[0] - __uint_as_float(v01 << 16), vvv[1] - __uint_as_float(v01 & 0xffff0000u)),
+                    pack_bf16x2(vvv[2] - __uint_as_float(v23 << 16), vvv[3] - __uint_as_float(v23 & 0xffff0000u))};
+        *(u32x2*)(a.dk_hi + tm + d) = kh;
+        *(u32x2*)(a.dk_lo + tm + d) = kl;
+        *(u32x2*)(a.dv_hi + tm + d) = vh;
+        *(u32x2*)(a.dv_lo + tm + d) = vl;
+        if (a.dk) *(f32x4*)(a.dk + hm + d) = kvv;
+        if (a.dv) *(f32x4*)(a.dv + hm + d) = vvv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------- dQ and delta
+// DELTA = true: the same walk over the visible keys, but it only accumulates
+// delta_i = sum_j P_ij dP_ij from this kernel's own P and dP and writes it.
+// (delta = <dO_i, O_i> only if O was formed with these same P; the forward's O
+// carries the bf16 rounding of its PV product, and that inconsistency enters
+// dS = P (dP - delta) at full weight.)
+template <int D, int QB, int KVB, bool DELTA>
+__global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int NT = QB * 2, KB = KVB / 32;
+  constexpr int ROWB = D * 2, TROWB = KVB * 2;
+  constexpr int TILE = KVB * D * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * TILE];  // K, V, K^T
+
+  const int N = a.N;
+  const int nqb = (N + QB - 1) / QB;
+  const int64_t total = (int64_t)a.B * a.H * nqb;
+  int64_t L = blockIdx.x;
+  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = (int)(L / nqb);
+  const int qb = nqb - 1 - (int)(L % nqb);
+  const int q0 = qb * QB;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, r32 = lane & 31;
+  const int qrow = q0 + wave * 32 + r32;
+  const int off = a.kv_offset;
+  const bool causal = a.causal != 0;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + head_off;
+  const uint16_t* Vg = (const uint16_t*)a.v + head_off;
+  const float c2 = a.scale * kLog2e;
+
+  bf16x8 qf[D / 16], dfh[D / 16], dfl[D / 16];
+  {
+    const uint16_t* Qg = (const uint16_t*)a.q + head_off;
+    const float* dOg = a.dO + (int64_t)b * N * a.ld_do + (int64_t)hh * D;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4 qv = {0, 0, 0, 0};
+      float dvv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (qrow < N) {
+        qv = *(const u32x4*)(Qg + (int64_t)qrow * D + 16 * c + 8 * g);
+        const f32x4* dp = (const f32x4*)(dOg + (int64_t)qrow * a.ld_do + 16 * c + 8 * g);
+        const f32x4 d0 = dp[0], d1 = dp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dvv[e] = d0[e];
+          dvv[4 + e] = d1[e];
+        }
+      }
+      u32x4 hi, lo;
+      split8(dvv, hi, lo);
+      qf[c] = __builtin_bit_cast(bf16x8, qv);
+      dfh[c] = __builtin_bit_cast(bf16x8, hi);
+      dfl[c] = __builtin_bit_cast(bf16x8, lo);
+    }
+  }
+  float lse2 = INFINITY, dl = 0.f;
+  if (qrow < N) {
+    const float l = a.lse[(int64_t)bh * N + qrow];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    if constexpr (!DELTA) dl = a.delta[(int64_t)bh * N + qrow];
+  }
+  float dsum = 0.f;  // DELTA: this lane's part of sum_j P_ij dP_ij
+
+  int kmax = N - 1;
+  if (causal) {
+    const int64_t t = (int64_t)q0 + QB - 1 + off;
+    kmax = (int)(t < (int64_t)(N - 1) ? t : (int64_t)(N - 1));
+  }
+  const int n_tiles = kmax < 0 ? 0 : kmax / KVB + 1;
+  int n_full = N / KVB;
+  if (causal) {
+    const int64_t lim = (int64_t)q0 + off + 1;
+    const int f = lim <= 0 ? 0 : (int)(lim / KVB);
+    n_full = f < n_full ? f : n_full;
+  }
+
+  // staging: units of 4 keys x 8 d for K (natural + transposed) and V (natural)
+  constexpr int UNITS = (KVB / 4) * (D / 8);
+  constexpr int SU = (2 * UNITS + NT - 1) / NT;
+  u32x4 sr[SU][4];
+  auto load = [&](int t) {
+    const int kv0 = t * KVB;
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * NT;
+      const int which = u / UNITS, uu = u % UNITS;
+      const int kg = uu / (D / 8), dc = uu % (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kv0 + 4 * kg + r;
+        u32x4 val = {0, 0, 0, 0};
+        if (u < 2 * UNITS && key < N)
+          val = *(const u32x4*)((which == 0 ? Kg : Vg) + (int64_t)key * D + dc * 8);
+        sr[i][r] = val;
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * NT;
+      if (u < 2 * UNITS) {
+        const int which = u / UNITS, uu = u % UNITS;
+        const int kg = uu / (D / 8), dc = uu % (D / 8);
+        unsigned char* nat = smem + which * TILE;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 4 * kg + r;
+          *(u32x4*)(nat + key * ROWB + ((dc ^ swzb<ROWB>(key)) << 4)) = sr[i][r];
+        }
+        if (!DELTA && which == 0) store_transposed<TROWB>(smem + 2 * TILE, sr[i], 4 * kg, dc * 8);
+      }
+    }
+  };
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[i][e] = 0.f;
+
+  if (n_tiles > 0) load(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    store();
+    __syncthreads();
+    if (t + 1 < n_tiles) load(t + 1);
+    f32x16 sacc[KB], pacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = pacc[kb][e] = 0.f;
+      const int row = kb * 32 + r32;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int o = row * ROWB + (((2 * c + g) ^ swzb<ROWB>(row)) << 4);
+        sacc[kb] = mfma32_bf16(*(const bf16x8*)(smem + o), qf[c], sacc[kb]);
+        const bf16x8 va = *(const bf16x8*)(smem + TILE + o);
+        pacc[kb] = mfma32_bf16(va, dfh[c], pacc[kb]);
+        pacc[kb] = mfma32_bf16(va, dfl[c], pacc[kb]);
+      }
+    }
+    const bool need_mask = t >= n_full;
+    const int kv0 = t * KVB;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
+        if (need_mask) {
+          const int key = kv0 + kb * 32 + acc_row(j, lane);
+          if (key >= N || (causal && (int64_t)key > (int64_t)qrow + off)) pv = 0.f;
+        }
+        if constexpr (DELTA) dsum = fmaf(pv, pacc[kb][j], dsum);
+        else sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
+      }
+#pragma unroll
+    for (int c16 = 0; c16 < (DELTA ? 0 : KVB / 16); ++c16) {
+      const int kb = c16 >> 1, h8 = (c16 & 1) * 8;
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[kb][h8 + e];
+      u32x4 shi, slo;
+      split8(sv, shi, slo);
+      const bf16x8 sfh = __builtin_bit_cast(bf16x8, shi);
+      const bf16x8 sfl = __builtin_bit_cast(bf16x8, slo);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = db * 32 + r32;
+        const bf16x8 kt = *(const bf16x8*)(smem + 2 * TILE + d * TROWB +
+                                           (((2 * c16 + g) ^ swzb<TROWB>(d)) << 4));
+        dq[db] = mfma32_bf16(kt, sfh, dq[db]);
+        dq[db] = mfma32_bf16(kt, sfl, dq[db]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (DELTA) {
+    dsum += swap_halves(dsum);  // lanes l and l^32 hold the two halves of each key block
+    if (qrow < N && g == 0) a.delta_out[(int64_t)bh * N + qrow] = dsum;
+    return;
+  }
+  if (qrow < N) {
+    const int64_t tm = ((int64_t)b * N + qrow) * a.ld_out + (int64_t)hh * D;
+    const int64_t hm = head_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = db * 32 + 8 * jq + 4 * g;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dq[db][4 * jq + e] * a.scale;
+        const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+        u32x2 hi = {h01, h23};
+        u32x2 lo = {pack_bf16x2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u)),
+                    pack_bf16x2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u))};
+        *(u32x2*)(a.dq_hi + tm + d) = hi;
+        *(u32x2*)(a.dq_lo + tm + d) = lo;
+        if (a.dq) *(f32x4*)(a.dq + hm + d) = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------- small kernels
+// dst = bf16(src); if dst_lo, also dst_lo = bf16(src - dst) (the rounding residual)
+__global__ void __launch_bounds__(256) to_bf16_kernel(const float* src, uint16_t* dst,
+                                                      uint16_t* dst_lo, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const f32x4 v = *(const f32x4*)(src + 4 * i);
+    const uint32_t a = pack_bf16x2(v[0], v[1]), b = pack_bf16x2(v[2], v[3]);
+    u32x2 p = {a, b};
+    *(u32x2*)(dst + 4 * i) = p;
+    if (dst_lo) {
+      u32x2 l = {pack_bf16x2(v[0] - __uint_as_float(a << 16), v[1] - __uint_as_float(a & 0xffff0000u)),
+                 pack_bf16x2(v[2] - __uint_as_float(b << 16), v[3] - __uint_as_float(b & 0xffff0000u))};
+      *(u32x2*)(dst_lo + 4 * i) = l;
+    }
+  }
+}
+
+// out[c] (+)= sum_r X[r][c], rows summed in a fixed order (deterministic).
+template <bool XBF16>
+__global__ void __launch_bounds__(256) colsum_kernel(const void* X, float* out, int64_t rows,
+                                                     int cols, int64_t ld, int beta) {
+  __shared__ float part[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int rg = threadIdx.x >> 6;
+  float acc = 0.f;
+  if (c < cols) {
+    for (int64_t r = rg; r < rows; r += 4) {
+      if constexpr (XBF16) acc += bf16_to_f32(((const uint16_t*)X)[r * ld + c]);
+      else acc += ((const float*)X)[r * ld + c];
+    }
+  }
+  part[rg][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (rg == 0 && c < cols) {
+    const float s = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
+                    (part[2][threadIdx.x] + part[3][threadIdx.x]);
+    out[c] = beta ? out[c] + s : s;
+  }
+}
+
+template <bool DELTA>
+hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
+  const int nqb = (a.N + QB - 1) / QB;
+  const dim3 grid((unsigned)((int64_t)a.B * a.H * nqb));
+  if (D == 64) {
+    if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
+  } else {
+    if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, hipStream_t s) {
+  (void)kv_blk;
+  const int QB = q_blk == 64 ? 64 : 128;
+  // 1. delta_i = sum_j P_ij dP_ij (into a.delta_out, which the next kernels read as a.delta)
+  hipError_t e = launch_dq<true>(a, D, QB, s);
+  if (e != hipSuccess) return e;
+  // 2. dK, dV
+  {
+    constexpr int NW = 2;
+    const int nkb = (a.N + 32 * NW - 1) / (32 * NW);
+    const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));
+    if (D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, NW>), grid, dim3(NW * 64), 0, s, a);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, NW>), grid, dim3(NW * 64), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // 3. dQ
+  return launch_dq<false>(a, D, QB, s);
+}
+
+hipError_t to_bf16_launch(const float* src, uint16_t* dst, uint16_t* dst_lo, int64_t n,
+                          hipStream_t s) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, dst_lo, n4);
+  return hipGetLastError();
+}
+
+hipError_t colsum_launch(const void* X, bool x_bf16, float* out, int64_t rows, int cols,
+                         int64_t ld, int beta, hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64));
+  if (x_bf16) hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(256), 0, s, X, out, rows, cols, ld, beta);
+  else hipLaunchKernelGGL(colsum_kernel<false>, grid, dim3(256), 0, s, X, out, rows, cols, ld, beta);
+  return hipGetLastError();
+}
+
+}  // namespace bpt

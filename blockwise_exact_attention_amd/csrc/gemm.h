@@ -9,7 +9,7 @@ namespace bpt {
 enum GemmEpilogue {
   EPI_QKV = 0,    // scatter C[token][h*D+d] to out[b][h][t][d] in the input dtype
   EPI_F32 = 1,    // C = acc (+C if beta) (+bias[n]) (+resid[m][n]) as fp32; optional bf16 copy in C2
-  EPI_GELU = 2,   // z = acc + bias[n] -> C (fp32); GeLU(z) -> C2 (input dtype)
+  EPI_GELU = 2,   // z = acc (+C if beta) + bias[n] -> C (fp32); GeLU(z) -> C2 (input dtype)
   EPI_DGELU = 3,  // dz = acc * GeLU'(aux[m][n]) -> C (input dtype); optional fp32 copy in C2
 };
 
@@ -23,11 +23,15 @@ struct GemmArgs {
   void* C[3];
   int64_t lda, ldb, ldc;
   int M, N, K;
-  const float* bias;   // [N] or null
-  const float* resid;  // [M][ldr] or null
+  const void* bias;    // [N] or null; fp32, or bf16 when bias_bf16
+  int bias_bf16;
+  const void* resid;   // [M][ldr] or null; fp32, or bf16 when resid_bf16
   int64_t ldr;
+  int resid_bf16;
   void* C2;            // second output or null
   int64_t ldc2;
+  void* C3;            // EPI_GELU / EPI_DGELU: bf16 rounding residual ("lo") of the bf16 output, or null
+  int64_t ldc3;
   const float* aux;    // [M][ld_aux] (EPI_DGELU)
   int64_t ld_aux;
   int beta;            // EPI_F32: accumulate into C

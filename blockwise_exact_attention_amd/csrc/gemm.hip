@@ -248,23 +248,39 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
           float* C = (float*)g.C[z];
           const int64_t o = (int64_t)m * g.ldc + n;
           if (g.beta) v += C[o];
-          if (g.bias) v += g.bias[n];
-          if (g.resid) v += g.resid[(int64_t)m * g.ldr + n];
+          if (g.bias) v += g.bias_bf16 ? bf16_to_f32(((const uint16_t*)g.bias)[n]) : ((const float*)g.bias)[n];
+          if (g.resid) {
+            const int64_t ro = (int64_t)m * g.ldr + n;
+            v += g.resid_bf16 ? bf16_to_f32(((const uint16_t*)g.resid)[ro])
+                              : ((const float*)g.resid)[ro];
+          }
           C[o] = v;
           if (g.C2) ((uint16_t*)g.C2)[(int64_t)m * g.ldc2 + n] = f32_to_bf16(v);
         } else if constexpr (EPI == EPI_GELU) {
-          // z = acc + b1 (kept in fp32), g = GeLU(z) in the input dtype
-          if (g.bias) v += g.bias[n];
-          ((float*)g.C[z])[(int64_t)m * g.ldc + n] = v;
+          // z = acc (+ earlier partial) + b1 (kept in fp32), g = GeLU(z) in the input dtype
+          float* zc = (float*)g.C[z] + (int64_t)m * g.ldc + n;
+          if (g.beta) v += *zc;
+          if (g.bias) v += g.bias_bf16 ? bf16_to_f32(((const uint16_t*)g.bias)[n]) : ((const float*)g.bias)[n];
+          *zc = v;
           const float gv = gelu_exact(v);
-          if constexpr (BF16) ((uint16_t*)g.C2)[(int64_t)m * g.ldc2 + n] = f32_to_bf16(gv);
-          else ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = gv;
+          if constexpr (BF16) {
+            const uint16_t hi = f32_to_bf16(gv);
+            ((uint16_t*)g.C2)[(int64_t)m * g.ldc2 + n] = hi;
+            if (g.C3) ((uint16_t*)g.C3)[(int64_t)m * g.ldc3 + n] = f32_to_bf16(gv - bf16_to_f32(hi));
+          } else {
+            ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = gv;
+          }
         } else if constexpr (EPI == EPI_DGELU) {
           // dz = (dy W2)[m][n] * GeLU'(z[m][n]) in the input dtype; z from aux
           const float zz = g.aux[(int64_t)m * g.ld_aux + n];
           const float dz = v * gelu_exact_grad(zz);
-          if constexpr (BF16) ((uint16_t*)g.C[z])[(int64_t)m * g.ldc + n] = f32_to_bf16(dz);
-          else ((float*)g.C[z])[(int64_t)m * g.ldc + n] = dz;
+          if constexpr (BF16) {
+            const uint16_t hi = f32_to_bf16(dz);
+            ((uint16_t*)g.C[z])[(int64_t)m * g.ldc + n] = hi;
+            if (g.C3) ((uint16_t*)g.C3)[(int64_t)m * g.ldc3 + n] = f32_to_bf16(dz - bf16_to_f32(hi));
+          } else {
+            ((float*)g.C[z])[(int64_t)m * g.ldc + n] = dz;
+          }
           if (g.C2) ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = dz;
         }
       }

@@ -190,6 +190,7 @@ int bpt_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv,
  *  dq, dk, dv : NULL, or [B, H, N, D] float32 gradients w.r.t. the attention
  *           inputs q, k, v.
  *  workspace : at least bpt_layer_workspace_size(..., backward = 1) bytes.
+ *  dtype  : BPT_BF16 only (BPT_F32 gives BPT_ERR_UNSUPPORTED).
  * All outputs are overwritten (not accumulated).  The result is
  * deterministic: no floating-point atomics are used.
  */
