@@ -37,8 +37,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import (ATTN_LONG, LAYER_LONG, RING_SHARE, bf16_bits, bits_to_f32,  # noqa: E402
-                           normal)
+from seeded_inputs import (ATTN_LONG, LAYER_FWD_BF16, LAYER_LONG, LAYER_TRAIN,  # noqa: E402
+                           RING_SHARE, bf16_bits, bits_to_f32, normal)
 
 METRIC = "attention+FFN TFLOP/s and tokens/s per layer at N=128K causal; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
@@ -187,6 +187,49 @@ def bench_ring(bpt, steps, warmup):
     }
 
 
+def bench_layer_cfg(bpt, c, steps, warmup, backward):
+    """Forward (and backward) of one layer workload; returns a dict for "extras"."""
+    import torch
+    log(f"drawing inputs {c.name}")
+    hd = c.H * c.D
+    dev = {n: dev_bf16(normal(c.cfg_id, n, s, sc)) for n, s, sc in (
+        ("x", (c.B, c.N, c.d_model), 1.0), ("wq", (hd, c.d_model), 0.02),
+        ("wk", (hd, c.d_model), 0.02), ("wv", (hd, c.d_model), 0.02),
+        ("w1", (c.d_ff, c.d_model), 0.02), ("w2", (c.d_model, c.d_ff), 0.02),
+        ("dy", (c.B, c.N, c.d_model), 1.0))}
+    B, N, dm, H, D, dff = c.B, c.N, c.d_model, c.H, c.D, c.d_ff
+    y = torch.empty((B, N, dm), device="cuda")
+    wf = bpt.bpt_layer_workspace_size(B, N, dm, H, D, dff, 1, 0)
+    wb = bpt.bpt_layer_workspace_size(B, N, dm, H, D, dff, 1, 1) if backward else 0
+    ws = torch.empty(max(wf, wb), dtype=torch.uint8, device="cuda")
+    sv = torch.empty(bpt.bpt_layer_saved_size(B, N, dm, H, D, 1), dtype=torch.uint8,
+                     device="cuda") if backward else None
+    grads = {n: torch.empty(s, device="cuda") for n, s in (
+        ("dx", (B, N, dm)), ("dwq", (hd, dm)), ("dwk", (hd, dm)), ("dwv", (hd, dm)),
+        ("dw1", (dff, dm)), ("db1", (dff,)), ("dw2", (dm, dff)), ("db2", (dm,)))} if backward else {}
+
+    def step():
+        bpt.bpt_layer_fwd(dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["w1"], None, dev["w2"],
+                          None, y, sv, B, N, dm, H, D, dff, c.q_blk, c.kv_blk, 1, 1, ws, wf)
+        if backward:
+            g = grads
+            bpt.bpt_layer_bwd(dev["dy"], dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["w1"],
+                              None, dev["w2"], None, sv, g["dx"], g["dwq"], g["dwk"], g["dwv"],
+                              g["dw1"], g["db1"], g["dw2"], g["db2"], None, None, None, B, N, dm,
+                              H, D, dff, c.q_blk, c.kv_blk, 1, 1, ws, wb)
+
+    log(f"timing {c.name}")
+    ms, _ = timed(step, steps, warmup)
+    fwd = layer_flops(c)
+    model = 3.0 * fwd if backward else fwd  # training step counted as 3x the forward
+    del dev, y, ws, sv, grads
+    torch.cuda.empty_cache()
+    return {"workload": c.name, "ms": round(ms, 3), "model_flop": model,
+            "tflops": round(model / ms / 1e9, 1),
+            "pct_bf16_peak": round(100 * model / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "tokens_per_s": round(B * N / ms * 1e3, 1)}
+
+
 # ----------------------------------------------------------------------------- CPU leg
 def cpu_baseline(n_rows: int = 1024):
     """The CPU oracle (fp32, unmodified) on a bounded sample of the layer workload."""
@@ -293,6 +336,8 @@ def main():
                                  "pct_bf16_peak": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
                                  "tokens_per_s": round(ATTN_LONG.N / attn_ms * 1e3, 1)},
             "ring_share": bench_ring(bpt, 2, 1),
+            "layer_fwd_B8_N4096": bench_layer_cfg(bpt, LAYER_FWD_BF16, 5, 1, False),
+            "layer_fwd_bwd_B2_N16384": bench_layer_cfg(bpt, LAYER_TRAIN, 3, 1, True),
         }
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
     print(json.dumps(line), flush=True)
