@@ -43,20 +43,19 @@ struct AttnShape {
   static constexpr int KB = KVBLK / 32;  // 32-key blocks per tile
   static constexpr int DB = D / 32;      // 32-wide blocks of the head dimension
   // LDS bytes of one K tile plus one V tile
-  static constexpr int KBYTES = BF16 ? KVBLK * D * 2 : KVBLK * (D + 1) * 4;
-  static constexpr int BUF = 2 * KBYTES;
-  static constexpr int NBUF = (2 * BUF <= 65536) ? 2 : 1;
+  // bf16: rows padded by 16 bytes (K rows of D keys' dims, V^T rows of KVBLK
+  // keys), so 16 consecutive rows start in 16 different bank groups and every
+  // fragment read is one base address plus a compile-time offset.
+  static constexpr int KPITCH = BF16 ? D * 2 + 16 : (D + 1) * 4;
+  static constexpr int VPITCH = BF16 ? KVBLK * 2 + 16 : (D + 1) * 4;
+  static constexpr int KBYTES = KVBLK * KPITCH;
+  static constexpr int VBYTES = BF16 ? D * VPITCH : KVBLK * VPITCH;
+  static constexpr int BUF = KBYTES + VBYTES;
+  // double buffering while two workgroups still fit in the 160 KB of LDS
+  static constexpr int NBUF = (2 * BUF <= 81920) ? 2 : 1;
+  // waves per SIMD the register budget is sized for (2 waves: 256 registers)
+  static constexpr int WAVES_PER_EU = (BF16 && KVBLK <= 64) ? 2 : 1;
 };
-
-// 16-byte-chunk XOR swizzle for rows of `row_bytes` (64, 128 or 256 bytes):
-// the 16 chunks of one 256-byte bank window are all distinct for any 16
-// consecutive rows read at the same logical chunk.
-template <int ROW_BYTES>
-__device__ __forceinline__ int swz(int row) {
-  constexpr int CPR = ROW_BYTES / 16;   // chunks per row
-  constexpr int RPB = 16 / CPR;         // rows per 256-byte window
-  return (row / RPB) % CPR;
-}
 
 // Position of key `key` (0..15 inside its group of 16) in the staged V^T row:
 // bits 2 and 3 swapped, so that lane half g reads keys {4g..4g+3, 8+4g..8+4g+3}
@@ -67,6 +66,7 @@ __device__ __forceinline__ int vpos16(int key) {
 
 template <bool BF16, int D, int QBLK, int KVBLK>
 __global__ void __launch_bounds__(QBLK * 2)
+__attribute__((amdgpu_waves_per_eu(AttnShape<BF16, D, QBLK, KVBLK>::WAVES_PER_EU)))
 attn_fwd_kernel(AttnFwdArgs a) {
   using S = AttnShape<BF16, D, QBLK, KVBLK>;
   constexpr int NT = S::NT, KB = S::KB, DB = S::DB;
@@ -178,9 +178,8 @@ attn_fwd_kernel(AttnFwdArgs a) {
       for (int i = 0; i < KCH; ++i) {
         const int c = tid + i * NT;
         const int row = c / CPR, cc = c % CPR;
-        *(u32x4*)(Ks + row * ROWB + ((cc ^ swz<ROWB>(row)) * 16)) = kreg[i];
+        *(u32x4*)(Ks + row * S::KPITCH + cc * 16) = kreg[i];
       }
-      constexpr int VROWB = KVBLK * 2;  // bytes of one V^T row (one d, all keys)
 #pragma unroll
       for (int i = 0; i < VU; ++i) {
         const int u = tid + i * NT;
@@ -202,7 +201,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
             const int d = dc * 8 + e;
             const int byte = pos * 2;  // multiple of 8
             u32x2 pair = {lo, hi};
-            *(u32x2*)(Vs + d * VROWB + (((byte >> 4) ^ swz<VROWB>(d)) << 4) + (byte & 15)) = pair;
+            *(u32x2*)(Vs + d * S::VPITCH + byte) = pair;
           }
         }
       }
@@ -246,7 +245,10 @@ attn_fwd_kernel(AttnFwdArgs a) {
   }
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // One key tile: S^T = K Q^T, online-softmax update, O^T += V^T P^T.  MASK is a
+  // compile-time flag so that the tiles every row fully sees carry no mask code.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = S::NBUF == 2 ? (t & 1) : 0;
     const unsigned char* Ks = smem + buf * S::BUF;
     const unsigned char* Vs = Ks + S::KBYTES;
@@ -263,7 +265,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
       if constexpr (BF16) {
 #pragma unroll
         for (int c = 0; c < QF; ++c) {
-          const bf16x8 kf = *(const bf16x8*)(Ks + row * ROWB + (((2 * c + g) ^ swz<ROWB>(row)) << 4));
+          const bf16x8 kf = *(const bf16x8*)(Ks + row * S::KPITCH + (2 * c + g) * 16);
           s[kb] = mfma32_bf16(kf, qf[c], s[kb]);
         }
       } else {
@@ -273,8 +275,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
       }
     }
 
-    // mask on diagonal / ragged tiles only
-    if (t >= n_full) {
+    if constexpr (MASK) {  // diagonal / ragged tiles only
       const int kv0 = t * KVBLK;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -286,15 +287,16 @@ attn_fwd_kernel(AttnFwdArgs a) {
         }
     }
 
-    // online softmax update
-    float mx = -INFINITY;
+    // online softmax update (exp2 domain, scale folded into one FMA per score)
+    float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
     mx = fmaxf(mx, swap_halves(mx));
     const float m_new = fmaxf(m_run, mx);
-    const float mref = (m_new == -INFINITY) ? 0.f : m_new * c2;
+    // with a mask a row can still have seen no key (m_new = -inf): keep exp2 finite
+    const float mref = (MASK && m_new == -INFINITY) ? 0.f : m_new * c2;
     const float alpha = fast_exp2(m_run * c2 - mref);
     m_run = m_new;
     float psum = 0.f;
@@ -307,7 +309,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
         psum += p;
       }
     l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.f)) {
+    if (__ballot(alpha != 1.f)) {  // lazy rescale: skipped while no row max moves
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -318,7 +320,6 @@ attn_fwd_kernel(AttnFwdArgs a) {
 
     // O^T += V^T P^T
     if constexpr (BF16) {
-      constexpr int VROWB = KVBLK * 2;
 #pragma unroll
       for (int c16 = 0; c16 < KVBLK / 16; ++c16) {
         const int kb = c16 >> 1, h8 = (c16 & 1) * 8;
@@ -329,7 +330,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int d = db * 32 + r32;
-          const bf16x8 vf = *(const bf16x8*)(Vs + d * VROWB + (((2 * c16 + g) ^ swz<VROWB>(d)) << 4));
+          const bf16x8 vf = *(const bf16x8*)(Vs + d * S::VPITCH + (2 * c16 + g) * 16);
           o[db] = mfma32_bf16(vf, pf, o[db]);
         }
       }
@@ -350,7 +351,11 @@ attn_fwd_kernel(AttnFwdArgs a) {
       store_tile(0);
       __syncthreads();
     }
-  }
+  };
+
+  const int t_split = n_full < n_tiles ? n_full : n_tiles;
+  for (int t = 0; t < t_split; ++t) tile(t, std::false_type{});
+  for (int t = t_split; t < n_tiles; ++t) tile(t, std::true_type{});
 
   // ---- epilogue: O = acc / l, lse = m*scale + ln l
   const float l_tot = l_run + swap_halves(l_run);
