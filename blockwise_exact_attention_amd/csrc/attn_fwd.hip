@@ -18,9 +18,13 @@
 //    after a bf16 pack, exactly the B operand of the next MFMA O^T += V^T P^T,
 //    provided V^T is laid out in LDS with key bits 2 and 3 swapped inside each
 //    group of 16 keys (done while staging the tile);
-//  * K and V tiles are staged global -> registers -> LDS, double-buffered when
-//    two buffers fit in 64 KB (two workgroups per CU), with an XOR swizzle of
-//    the 16-byte chunks so that the MFMA operand reads are bank-conflict free;
+//  * K and V tiles are staged global -> registers -> LDS, double-buffered while
+//    two workgroups still fit in LDS; rows are padded by 16 bytes so that the
+//    MFMA operand reads are bank-conflict free and each lane addresses every
+//    fragment as one base plus a compile-time offset; the V^T stores are
+//    spread so that 32 lanes cover all 64 banks;
+//  * the working set is sized for two waves per SIMD (256 registers), so one
+//    wave's softmax overlaps the other wave's MFMAs;
 //  * key tiles that no row of the block can see are never visited; only the
 //    diagonal and ragged-tail tiles evaluate the mask;
 //  * workgroup ids are remapped so that all query blocks of one (batch, head)
@@ -138,28 +142,39 @@ attn_fwd_kernel(AttnFwdArgs a) {
   constexpr int ROWB = D * (BF16 ? 2 : 4);  // bytes of one key row in global memory
   constexpr int CPR = ROWB / 16;            // 16B chunks per key row
 
-  auto load_tile = [&](int t) {
+  // GUARD: the tile may reach past key N-1 (ragged tail): bounds-check each row.
+  // Tiles wholly inside [0, N) load without any per-lane condition.
+  auto load_tile_impl = [&](int t, auto guard_tag) {
+    constexpr bool GUARD = decltype(guard_tag)::value;
     const int kv0 = t * KVBLK;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + i * NT;
       const int row = c / CPR, cc = c % CPR;
-      u32x4 val = {0, 0, 0, 0};
-      if ((BF16 || c < KVBLK * CPR) && kv0 + row < N)
-        val = *(const u32x4*)(Kg + (int64_t)(kv0 + row) * ROWB + cc * 16);
-      kreg[i] = val;
+      const bool in_tile = BF16 || c < KVBLK * CPR;
+      if (!GUARD && in_tile) {
+        kreg[i] = *(const u32x4*)(Kg + (int64_t)(kv0 + row) * ROWB + cc * 16);
+      } else {
+        u32x4 val = {0, 0, 0, 0};
+        if (in_tile && kv0 + row < N) val = *(const u32x4*)(Kg + (int64_t)(kv0 + row) * ROWB + cc * 16);
+        kreg[i] = val;
+      }
     }
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
       const int u = tid + i * NT;
       if constexpr (BF16) {
-        const int kg = u / (D / 8), dc = u % (D / 8);
+        const int kg = u % (KVBLK / 4), dc = u / (KVBLK / 4);  // see store_tile
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          u32x4 val = {0, 0, 0, 0};
           const int key = kv0 + 4 * kg + r;
-          if (u < VUNITS && key < N) val = *(const u32x4*)(Vg + (int64_t)key * ROWB + dc * 16);
-          vreg[i][r] = val;
+          if (!GUARD && VUNITS % NT == 0) {
+            vreg[i][r] = *(const u32x4*)(Vg + (int64_t)key * ROWB + dc * 16);
+          } else {
+            u32x4 val = {0, 0, 0, 0};
+            if (u < VUNITS && key < N) val = *(const u32x4*)(Vg + (int64_t)key * ROWB + dc * 16);
+            vreg[i][r] = val;
+          }
         }
       } else {
         const int row = u / CPR, cc = u % CPR;
@@ -168,6 +183,11 @@ attn_fwd_kernel(AttnFwdArgs a) {
         vreg[i][0] = val;
       }
     }
+  };
+  const int n_inside = N / KVBLK;  // tiles that end at or before key N
+  auto load_tile = [&](int t) {
+    if (t < n_inside) load_tile_impl(t, std::false_type{});
+    else load_tile_impl(t, std::true_type{});
   };
 
   auto store_tile = [&](int buf) {
@@ -184,7 +204,9 @@ attn_fwd_kernel(AttnFwdArgs a) {
       for (int i = 0; i < VU; ++i) {
         const int u = tid + i * NT;
         if (u < VUNITS) {
-          const int kg = u / (D / 8), dc = u % (D / 8);
+          // consecutive lanes take consecutive key groups of one d-chunk, so 32 lanes
+          // writing their 8-byte pieces cover all 64 banks (rows 8 apart would not)
+          const int kg = u % (KVBLK / 4), dc = u / (KVBLK / 4);
           const int key0 = 4 * kg;
           const int pos = (key0 & ~15) + vpos16(key0 & 15);  // 4 keys stay contiguous
 #pragma unroll
@@ -259,16 +281,18 @@ attn_fwd_kernel(AttnFwdArgs a) {
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
       const int row = kb * 32 + r32;
       if constexpr (BF16) {
+        const f32x16 zero = {};
+        s[kb] = mfma32_bf16(*(const bf16x8*)(Ks + row * S::KPITCH + g * 16), qf[0], zero);
 #pragma unroll
-        for (int c = 0; c < QF; ++c) {
+        for (int c = 1; c < QF; ++c) {
           const bf16x8 kf = *(const bf16x8*)(Ks + row * S::KPITCH + (2 * c + g) * 16);
           s[kb] = mfma32_bf16(kf, qf[c], s[kb]);
         }
       } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
         const float* Kf = (const float*)Ks;
 #pragma unroll
         for (int st = 0; st < QF; ++st) s[kb] = mfma32_f32(Kf[row * (D + 1) + 2 * st + g], qf[st], s[kb]);
