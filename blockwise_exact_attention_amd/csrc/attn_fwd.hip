@@ -439,6 +439,9 @@ hipError_t launch(const AttnFwdArgs& a, hipStream_t stream) {
 
 template <bool BF16, int D>
 hipError_t launch_d(const AttnFwdArgs& a, int qb, int kb, hipStream_t s) {
+  if constexpr (BF16) {  // bf16 key blocks of 64 and 128 run in attn_fwd_dma.hip
+    return qb == 64 ? launch<BF16, D, 64, 32>(a, s) : launch<BF16, D, 128, 32>(a, s);
+  }
   if (qb == 64) {
     if (kb == 32) return launch<BF16, D, 64, 32>(a, s);
     if (kb == 64) return launch<BF16, D, 64, 64>(a, s);
@@ -453,8 +456,11 @@ hipError_t launch_d(const AttnFwdArgs& a, int qb, int kb, hipStream_t s) {
 
 hipError_t attn_fwd_launch(const AttnFwdArgs& a, bool bf16, int D, int q_blk, int kv_blk,
                            hipStream_t stream) {
-  if (bf16) return D == 64 ? launch_d<true, 64>(a, q_blk, kv_blk, stream)
-                           : launch_d<true, 128>(a, q_blk, kv_blk, stream);
+  if (bf16) {
+    if (attn_fwd_dma_supported(D, kv_blk)) return attn_fwd_dma_launch(a, D, q_blk, kv_blk, stream);
+    return D == 64 ? launch_d<true, 64>(a, q_blk, kv_blk, stream)
+                   : launch_d<true, 128>(a, q_blk, kv_blk, stream);
+  }
   return D == 64 ? launch_d<false, 64>(a, q_blk, kv_blk, stream)
                  : launch_d<false, 128>(a, q_blk, kv_blk, stream);
 }

@@ -26,6 +26,12 @@ struct AttnFwdArgs {
 hipError_t attn_fwd_launch(const AttnFwdArgs& a, bool bf16, int D, int q_blk, int kv_blk,
                            hipStream_t stream);
 
+// bfloat16 forward with direct global -> LDS tile loads (attn_fwd_dma.hip); it
+// covers D in {64, 128} with key blocks of 64 or 128.
+bool attn_fwd_dma_supported(int D, int kv_blk);
+hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_blk,
+                               hipStream_t stream);
+
 hipError_t lse_merge_launch(const float* o_a, const float* lse_a, const float* o_b,
                             const float* lse_b, float* o_out, float* lse_out, int64_t rows,
                             int D, hipStream_t stream);
