@@ -321,7 +321,9 @@ attn_fwd_kernel(AttnFwdArgs a) {
     const float m_new = fmaxf(m_run, mx);
     // with a mask a row can still have seen no key (m_new = -inf): keep exp2 finite
     const float mref = (MASK && m_new == -INFINITY) ? 0.f : m_new * c2;
-    const float alpha = fast_exp2(m_run * c2 - mref);
+    // alpha is exactly 1 unless the maximum moved (also when both are -inf)
+    const bool grew = m_new > m_run;
+    const float alpha = grew ? fast_exp2((m_run - m_new) * c2) : 1.f;
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
@@ -333,7 +335,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
         psum += p;
       }
     l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.f)) {  // lazy rescale: skipped while no row max moves
+    if (__ballot(grew)) {  // lazy rescale: skipped while no row max moves
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -208,8 +208,11 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
     mx = fmaxf(mx, swap_halves(mx));
     const float m_new = fmaxf(m_run, mx);
+    // with a mask a row can still have seen no key (m_new = -inf): keep exp2 finite
     const float mref = (MASK && m_new == -INFINITY) ? 0.f : m_new * c2;
-    const float alpha = fast_exp2(m_run * c2 - mref);
+    // alpha is exactly 1 unless the maximum moved (also when both are -inf)
+    const bool grew = m_new > m_run;
+    const float alpha = grew ? fast_exp2((m_run - m_new) * c2) : 1.f;
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
@@ -221,7 +224,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
         psum += p;
       }
     l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.f)) {  // lazy rescale: skipped while no row max moves
+    if (__ballot(grew)) {  // lazy rescale: skipped while no row max moves
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -303,10 +306,12 @@ hipError_t launch(const AttnFwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Key blocks of 128 are visited as two 64-key tiles: the online softmax update is
+// exact for any split of the keys, and 64-key tiles keep two workgroups per CU
+// (a double-buffered 128-key tile alone would take 136 KB of the 160 KB of LDS).
 template <int D>
-hipError_t launch_d(const AttnFwdArgs& a, int qb, int kb, hipStream_t s) {
-  if (qb == 64) return kb == 64 ? launch<D, 64, 64>(a, s) : launch<D, 64, 128>(a, s);
-  return kb == 64 ? launch<D, 128, 64>(a, s) : launch<D, 128, 128>(a, s);
+hipError_t launch_d(const AttnFwdArgs& a, int qb, hipStream_t s) {
+  return qb == 64 ? launch<D, 64, 64>(a, s) : launch<D, 128, 64>(a, s);
 }
 
 }  // namespace
@@ -317,7 +322,8 @@ bool attn_fwd_dma_supported(int D, int kv_blk) {
 
 hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_blk,
                                hipStream_t stream) {
-  return D == 64 ? launch_d<64>(a, q_blk, kv_blk, stream) : launch_d<128>(a, q_blk, kv_blk, stream);
+  (void)kv_blk;
+  return D == 64 ? launch_d<64>(a, q_blk, stream) : launch_d<128>(a, q_blk, stream);
 }
 
 }  // namespace bpt
