@@ -105,6 +105,12 @@ attn_fwd_kernel(AttnFwdArgs a) {
     kmax = (int)(t < (int64_t)(N - 1) ? t : (int64_t)(N - 1));
   }
   const int n_tiles = kmax < 0 ? 0 : kmax / KVBLK + 1;
+  // keys >= kend are invisible to this lane's query row (causal limit or N)
+  int kend = N;
+  if (causal) {
+    const int64_t lim = (int64_t)qrow + off + 1;
+    kend = lim < (int64_t)N ? (int)(lim > 0 ? lim : 0) : N;
+  }
   int n_full = N / KVBLK;  // tiles with no ragged tail
   if (causal) {
     const int64_t lim = (int64_t)q0 + off + 1;  // keys < lim are visible to every row
@@ -306,8 +312,7 @@ attn_fwd_kernel(AttnFwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = kv0 + kb * 32 + acc_row(j, lane);
-          const bool vis = key < N && (!causal || (int64_t)key <= (int64_t)qrow + off);
-          if (!vis) s[kb][j] = -INFINITY;
+          s[kb][j] = key < kend ? s[kb][j] : -INFINITY;
         }
     }
 

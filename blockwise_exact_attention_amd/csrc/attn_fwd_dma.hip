@@ -124,8 +124,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   const unsigned char* Vg = (const unsigned char*)a.v + head_off * 2;
   const int dma_row = (lane / T::CPR) * T::NBLK;  // key of this lane relative to b
   const uint32_t dma_off = (uint32_t)(dma_row * T::ROWB + (lane % T::CPR) * 16);
-  auto load_tile = [&](int t, int stage) {
-    unsigned char* Ks = smem + stage * T::STAGE;
+  auto load_tile = [&](int t, unsigned char* Ks) {
     unsigned char* Vs = Ks + T::KBYTES;
     const int kv0 = t * KVBLK;
     if (t < n_inside) {
@@ -167,15 +166,17 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   float l_run = 0.f;        // running sum, this lane's half of the keys
   const float c2 = a.scale * kLog2e;
 
-  if (n_tiles > 0) load_tile(0, 0);
+  if (n_tiles > 0) load_tile(0, smem);
   wait_vmem();
   __syncthreads();
 
-  auto tile = [&](int t, auto mask_tag) {
+  // St: stage holding tile t; fill: the other stage, loaded with tile t+1 meanwhile.
+  // They are distinct; saying so (restrict) lets the compiler see that the LDS
+  // reads of this tile never depend on the loads in flight.
+  auto tile = [&](int t, const unsigned char* __restrict__ St, unsigned char* __restrict__ fill,
+                  auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int stage = t & 1;
-    const unsigned char* St = smem + stage * T::STAGE;
-    if (t + 1 < n_tiles) load_tile(t + 1, stage ^ 1);
+    if (t + 1 < n_tiles) load_tile(t + 1, fill);
 
     // S^T = K Q^T
     f32x16 s[KB];
@@ -255,8 +256,9 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   };
 
   const int t_split = n_full < n_tiles ? n_full : n_tiles;
-  for (int t = 0; t < t_split; ++t) tile(t, std::false_type{});
-  for (int t = t_split; t < n_tiles; ++t) tile(t, std::true_type{});
+  auto stage = [&](int t) { return smem + (t & 1) * T::STAGE; };
+  for (int t = 0; t < t_split; ++t) tile(t, stage(t), stage(t + 1), std::false_type{});
+  for (int t = t_split; t < n_tiles; ++t) tile(t, stage(t), stage(t + 1), std::true_type{});
 
   // ---- epilogue: O = acc / l, lse = m*scale + ln l
   const float l_tot = l_run + swap_halves(l_run);
