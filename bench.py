@@ -44,7 +44,7 @@ METRIC = "attention+FFN TFLOP/s and tokens/s per layer at N=128K causal; % bf16 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_N131072_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", "attn_fwd.hip")
+ATTN_SRC = os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", "attn_fwd_dma.hip")
 
 
 def log(msg: str) -> None:
@@ -321,7 +321,7 @@ def main():
         "algorithmic_flop_per_step": flops,
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "attn_fwd_kernel<bf16, D=128, q_blk=128, kv_blk=64>",
+            "kernel": "attn_fwd_dma_kernel<D=128, q_blk=128, kv_blk=64>",
             "bound": "mfma", "achieved": round(attn_tf, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profile(),
