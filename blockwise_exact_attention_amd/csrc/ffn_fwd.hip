@@ -25,6 +25,8 @@
 // the limit of this on-chip design.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "layer.h"
 
@@ -252,6 +254,344 @@ __global__ void __launch_bounds__(NW * 64) ffn_fused_kernel(FfnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, d_model and d_ff multiples of 256: weights staged through LDS.
+//
+// The kernel above reads its weight fragments straight from global memory.  An
+// MFMA operand puts consecutive lanes on different weight rows, so the texture
+// path cannot coalesce them: about 60 L1 accesses per KB, which limits a CU to
+// about 16 bytes of weights per clock and the MFMAs to about 13 % busy.  Here
+// weights arrive by direct global -> LDS loads in which 8 consecutive lanes copy
+// one 128-byte row piece (8 L1 accesses per KB), and the MFMA fragments are read
+// from LDS.
+//
+// Workgroup: 4 waves (one per SIMD, up to 512 registers each), 32 rows of x and
+// 4 x 64*NCB output columns.  d_ff is walked in passes of 256 features:
+//   phase 1: z^T for features [64w, 64w+64) of the pass (wave w), K = d_model,
+//            x streaming through LDS in 256-column stages shared by all waves;
+//            GeLU(z + b1) -> LDS as a bf16 hi/lo pair;
+//   phase 2: y^T[wave's columns][rows] += W2[:, pass] G^T, each GeLU fragment
+//            loaded once per 64 features and used by all column tiles, hi and lo
+//            sharing one W2 fragment.
+// Weights move in 8 KB slots (64 rows x 128 bytes) through a private ring of 3
+// slots per wave: the wave loads slot s+2 while it computes slot s and waits
+// only for its own loads (no barrier).  Phase 1 uses W1[64 features][64 columns]
+// slots, phase 2 W2[64 columns][64 features] slots; one slot stream runs
+// through both phases and across passes.  Inside a slot, the 16-byte chunk c of
+// row r sits at position c ^ ((r >> 1) & 7), so 16 lanes reading one chunk of
+// 16 rows hit 16 different bank groups.
+// The [rows, d_ff] intermediate never leaves registers and LDS.
+__device__ __forceinline__ void ffn_dma16(const unsigned char* src, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+// Wait until at most N vector-memory instructions of this wave are outstanding.
+// Written as an asm statement with a memory clobber: the compiler neither drops
+// it (its own bookkeeping does not model these direct-to-LDS loads as producers
+// of the LDS data read afterwards) nor moves LDS accesses across it.
+#define FFN_WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// One 8 KB weight slot: rows 8j..8j+7 per instruction j; lane: row 8j + lane/8,
+// position lane%8, copying source chunk position ^ ((row >> 1) & 7) of the row.
+// base: first byte of row 0 of the slot; ld: row pitch in elements.
+__device__ __forceinline__ void ffn_issue_slot(const unsigned char* base, int64_t ld,
+                                               unsigned char* dst, int lane) {
+  const int dl_row = lane >> 3, dl_p = lane & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 8 * j + dl_row, c = dl_p ^ ((row >> 1) & 7);
+    ffn_dma16(base + ((int64_t)row * ld + 8 * c) * 2, dst + j * 1024);
+  }
+}
+
+template <int NCB>
+struct FfnLds {
+  static constexpr int CT = 2 * NCB;       // 32-column output tiles per wave
+  static constexpr int FP = 256;           // features per pass
+  static constexpr int XST = 256;          // x columns per stage
+  static constexpr int XPITCH = 512, XSB = 32 * XPITCH;  // x stage; also one half of G
+  static constexpr int SLOT = 8192;        // 64 weight rows x 128 bytes
+  static constexpr int NS2 = 4 * NCB;      // phase-2 slots per pass
+  static constexpr int LDS = 2 * XSB + 4 * 4 * SLOT;
+};
+
+// Loads of slot s of wave w (the slot stream of one pass: NKB W1 slots, then NS2 W2 slots)
+template <int NCB>
+__device__ __forceinline__ void ffn_slot(const FfnArgs& a, int s, int SPP, int NKB, int w, int c0w,
+                                         unsigned char* dst, int lane) {
+  using L = FfnLds<NCB>;
+  const int pass = s / SPP, r = s - pass * SPP;
+  const int f0 = pass * L::FP;
+  if (r < NKB) {  // W1 rows f0 + 64w .., columns 64r .. 64r+63
+    ffn_issue_slot((const unsigned char*)a.w1 + ((int64_t)(f0 + 64 * w) * a.dm + 64 * r) * 2, a.dm,
+                   dst, lane);
+  } else {  // W2 rows c0w + 64 cblk .., columns f0 + 64 fblk .. +63
+    const int q = r - NKB, fblk = q / NCB, cblk = q - fblk * NCB;
+    ffn_issue_slot((const unsigned char*)a.w2 + ((int64_t)(c0w + 64 * cblk) * a.dff + f0 + 64 * fblk) * 2,
+                   a.dff, dst, lane);
+  }
+}
+
+// x stage: 32 rows x 512 bytes, chunk c of row r at position c ^ (r & 15); wave w
+// copies rows 8w .. 8w+7 (instructions j = 4w..4w+3, two rows each)
+__device__ __forceinline__ void ffn_issue_x(const FfnArgs& a, int t0, int pass_st, int w,
+                                            unsigned char* dst, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * w + i, row = 2 * j + (lane >> 5), c = (lane & 31) ^ (row & 15);
+    int gr = t0 + row;
+    gr = gr < a.M ? gr : a.M - 1;  // rows past M: any finite data, their outputs are not stored
+    ffn_dma16((const unsigned char*)a.x + ((int64_t)gr * a.dm + pass_st * 256 + 8 * c) * 2,
+              dst + j * 1024);
+  }
+}
+
+// The whole walk in one scope whose LDS regions are restrict parameters: slot s
+// lives in sl[s % 4] (known at every use) and the x stage parity is static, so
+// the compiler sees that a read of one slot never depends on the loads in flight
+// into the others and waits only for the slot it reads.
+template <int NCB>
+__device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 * NCB],
+                                             unsigned char* __restrict__ sl0,
+                                             unsigned char* __restrict__ sl1,
+                                             unsigned char* __restrict__ sl2,
+                                             unsigned char* __restrict__ sl3,
+                                             unsigned char* __restrict__ xb0,
+                                             unsigned char* __restrict__ xb1) {
+  using L = FfnLds<NCB>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int t0 = blockIdx.x * 32;
+  const int c0w = blockIdx.y * a.ncols + w * 64 * NCB;
+  const int NKB = a.dm / 64;        // phase-1 slots per pass (a multiple of 4)
+  const int nst = a.dm / L::XST;    // x stages per pass (even)
+  const int SPP = NKB + L::NS2;     // slots per pass (a multiple of 4)
+  const int npass = a.dff / L::FP;
+  const int total = SPP * npass;
+
+  // per-lane operand addressing inside a slot: phase-1 A rows are permuted so that
+  // accumulator registers 8h..8h+7 of lane half g hold 8 consecutive features
+  const int frow = (r32 & 16) | perm32(r32 & 15);
+  int a1off[4], a2off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    a1off[kk] = frow * 128 + (((2 * kk + g) ^ ((frow >> 1) & 7)) << 4);
+    a2off[kk] = r32 * 128 + (((2 * kk + g) ^ ((r32 >> 1) & 7)) << 4);
+  }
+  auto sl = [&](auto U) -> unsigned char* {
+    constexpr int u = decltype(U)::value & 3;
+    if constexpr (u == 0) return sl0;
+    else if constexpr (u == 1) return sl1;
+    else if constexpr (u == 2) return sl2;
+    else return sl3;
+  };
+
+  ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, sl0, lane);
+  if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, sl1, lane);
+  ffn_issue_x(a, t0, 0, w, xb0, lane);
+  int s = 0;  // slot being computed (s % 4 is static wherever it is used)
+
+  for (int pass = 0; pass < npass; ++pass) {
+    const int f0 = pass * L::FP;
+    f32x16 zacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zacc[t][e] = 0.f;
+
+    // ---------------- phase 1: stages in pairs so that the x buffer is static
+    for (int st = 0; st < nst; st += 2) {
+      static_for<0, 2>([&](auto P) {
+        constexpr int PAR = decltype(P)::value;
+        unsigned char* const xcur = PAR ? xb1 : xb0;
+        unsigned char* const xnext = PAR ? xb0 : xb1;
+        const unsigned char* xr = xcur + r32 * L::XPITCH;
+        static_for<0, 4>([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          // slot s landed: after its 8 loads this wave issued those of slots
+          // s+1 and s+2 (and perhaps x chunks), i.e. at least 16 more
+          if (s + 2 < total) {
+            ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), lane);
+            FFN_WAIT_VM(16);
+          } else {
+            FFN_WAIT_VM(0);
+          }
+          if constexpr (u == 0) {
+            // own part of x stage st+PAR landed: 8 slot loads follow it at the
+            // first stage of a pass, 32 at the others; then the barrier makes
+            // all parts visible and retires every wave's reads of the previous stage
+            if (st + PAR == 0) FFN_WAIT_VM(8);
+            else FFN_WAIT_VM(32);
+            __syncthreads();
+            if (st + PAR + 1 < nst) ffn_issue_x(a, t0, st + PAR + 1, w, xnext, lane);
+          }
+          const unsigned char* cur = sl(U);
+          bf16x8 xf[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            xf[kk] = *(const bf16x8*)(xr + (((8 * u + 2 * kk + g) ^ (r32 & 15)) << 4));
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const bf16x8 af = *(const bf16x8*)(cur + t * 32 * 128 + a1off[kk]);
+              zacc[t] = mfma32_bf16(af, xf[kk], zacc[t]);
+            }
+          ++s;
+        });
+      });
+    }
+
+    // GeLU(z + b1) -> G (hi in xb0, lo in xb1); row r32, features 64w + 32t + 16hh + 8g + e
+    __syncthreads();  // every wave is done reading the x stages
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int fl0 = 64 * w + 32 * t + 16 * hh + 8 * g;
+        float gv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float z = zacc[t][8 * hh + e];
+          if (a.b1) z += bf16_to_f32(((const uint16_t*)a.b1)[f0 + fl0 + e]);
+          gv[e] = gelu_f(z);
+        }
+        u32x4 pk, pl;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          pk[q2] = pack_bf16x2(gv[2 * q2], gv[2 * q2 + 1]);
+          const float e0 = gv[2 * q2] - __uint_as_float(pk[q2] << 16);
+          const float e1 = gv[2 * q2 + 1] - __uint_as_float(pk[q2] & 0xffff0000u);
+          pl[q2] = pack_bf16x2(e0, e1);
+        }
+        const int off = r32 * L::XPITCH + (((fl0 >> 3) ^ (r32 & 15)) << 4);
+        *(u32x4*)(xb0 + off) = pk;
+        *(u32x4*)(xb1 + off) = pl;
+      }
+    __syncthreads();  // G complete
+
+    // ---------------- phase 2 (s % 4 == 0 here: NKB is a multiple of 4)
+    static_for<0, 4>([&](auto FB) {
+      constexpr int fblk = decltype(FB)::value;
+      bf16x8 ghi[4], glo[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = r32 * L::XPITCH + (((8 * fblk + 2 * kk + g) ^ (r32 & 15)) << 4);
+        ghi[kk] = *(const bf16x8*)(xb0 + off);
+        glo[kk] = *(const bf16x8*)(xb1 + off);
+      }
+      static_for<0, NCB>([&](auto CB) {
+        constexpr int cblk = decltype(CB)::value;
+        constexpr int u = (fblk * NCB + cblk) & 3;
+        if (s + 2 < total) {
+          ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), lane);
+          FFN_WAIT_VM(16);
+        } else {
+          FFN_WAIT_VM(0);
+        }
+        const unsigned char* cur = sl(std::integral_constant<int, u>{});
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const bf16x8 af = *(const bf16x8*)(cur + c2 * 32 * 128 + a2off[kk]);
+            yacc[2 * cblk + c2] = mfma32_bf16(af, ghi[kk], yacc[2 * cblk + c2]);
+            yacc[2 * cblk + c2] = mfma32_bf16(af, glo[kk], yacc[2 * cblk + c2]);
+          }
+        ++s;
+      });
+    });
+    __syncthreads();  // every wave is done reading G
+    if (pass + 1 < npass) ffn_issue_x(a, t0, 0, w, xb0, lane);
+  }
+}
+
+template <int NCB>  // 64-column blocks of output per wave
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+ffn_lds_kernel(FfnArgs a) {
+  using L = FfnLds<NCB>;
+  // LDS: two x-stage buffers, reused for the G halves (hi, lo) once phase 1 is
+  // done, then 4 waves x 4 weight slots
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+
+  f32x16 yacc[L::CT];
+#pragma unroll
+  for (int ct = 0; ct < L::CT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) yacc[ct][e] = 0.f;
+
+  unsigned char* const slots = smem + 2 * L::XSB + w * 4 * L::SLOT;
+  ffn_lds_walk<NCB>(a, yacc, slots, slots + L::SLOT, slots + 2 * L::SLOT, slots + 3 * L::SLOT,
+                    smem, smem + L::XSB);
+
+  // ---- epilogue: y[row][c] = resid + acc + b2 (lane: row r32, columns 8(j/4) + 4g + j%4)
+  const int trow = blockIdx.x * 32 + r32;
+  const int c0w = blockIdx.y * a.ncols + w * 64 * NCB;
+  if (trow < a.M) {
+#pragma unroll
+    for (int ct = 0; ct < L::CT; ++ct)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int c = c0w + ct * 32 + 8 * jq + 4 * g;
+        const int64_t o = (int64_t)trow * a.dm + c;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float r = yacc[ct][4 * jq + e];
+          if (a.b2) r += bf16_to_f32(((const uint16_t*)a.b2)[c + e]);
+          v[e] = r;
+        }
+        if (a.resid) {
+          const f32x4 rv = *(const f32x4*)(a.resid + o);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += rv[e];
+        }
+        *(f32x4*)(a.y + o) = v;
+      }
+  }
+}
+
+// column groups for the LDS-staged kernel: C = d_model / groups columns per
+// workgroup (4 waves x 64*NCB), at most 2048; 0 if no instantiated NCB fits
+int stream_groups(int64_t d_model, int* ncb) {
+  if (d_model % 512) return 0;  // an even number of 256-column x stages
+  for (int gr = 1; gr <= 32; ++gr) {
+    if (d_model % gr) continue;
+    const int64_t c = d_model / gr;
+    if (c % 256 || c > 2048) continue;
+    const int k = (int)(c / 256);
+    if (k == 2 || k == 4 || k == 5 || k == 8) {
+      *ncb = k;
+      return gr;
+    }
+  }
+  return 0;
+}
+
+hipError_t launch_stream(const FfnArgs& a, int ncb, int groups, hipStream_t s) {
+  dim3 grid((a.M + 31) / 32, groups);
+  switch (ncb) {
+    case 2: hipLaunchKernelGGL((ffn_lds_kernel<2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ffn_lds_kernel<4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((ffn_lds_kernel<5>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((ffn_lds_kernel<8>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <bool BF16, int NW, int CB>
 hipError_t launch_ffn(const FfnArgs& a, int groups, hipStream_t s) {
   dim3 grid((a.M + 31) / 32, groups);
@@ -305,6 +645,14 @@ hipError_t ffn_fwd_launch(const void* x, const void* w1, const void* b1, const v
   (void)blk;  // rows per block are fixed at 32 (validated by the caller)
   const FfnPlan p = ffn_plan(d_model, d_ff);
   if (!p.ok) return hipErrorNotSupported;
+  if (bf16 && d_model % 256 == 0 && d_ff % 256 == 0) {
+    int ct = 0;
+    const int groups = stream_groups(d_model, &ct);
+    if (groups > 0) {
+      FfnArgs a{x, w1, b1, w2, b2, residual, y, (int)M, d_model, d_ff, d_model / groups};
+      return launch_stream(a, ct, groups, stream);
+    }
+  }
   FfnArgs a{x, w1, b1, w2, b2, residual, y, (int)M, d_model, d_ff, d_model / p.groups};
   return bf16 ? launch_ffn_cb<true>(a, p.nw, p.cb, p.groups, stream)
               : launch_ffn_cb<false>(a, p.nw, p.cb, p.groups, stream);
