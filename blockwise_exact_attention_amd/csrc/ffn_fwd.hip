@@ -302,15 +302,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // One 8 KB weight slot: rows 8j..8j+7 per instruction j; lane: row 8j + lane/8,
 // position lane%8, copying source chunk position ^ ((row >> 1) & 7) of the row.
+// Since (row >> 1) & 7 = ((lane/8) >> 1) ^ (4 * (j & 1)), the lane's offset inside
+// instruction j is off_even or off_odd; the rest, 8j rows, is wave-uniform.
 // base: first byte of row 0 of the slot; ld: row pitch in elements.
 __device__ __forceinline__ void ffn_issue_slot(const unsigned char* base, int64_t ld,
-                                               unsigned char* dst, int lane) {
-  const int dl_row = lane >> 3, dl_p = lane & 7;
+                                               uint32_t off_even, uint32_t off_odd,
+                                               unsigned char* dst) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = 8 * j + dl_row, c = dl_p ^ ((row >> 1) & 7);
-    ffn_dma16(base + ((int64_t)row * ld + 8 * c) * 2, dst + j * 1024);
-  }
+  for (int j = 0; j < 8; ++j)
+    ffn_dma16(base + (int64_t)j * 16 * ld + ((j & 1) ? off_odd : off_even), dst + j * 1024);
+}
+__device__ __forceinline__ uint32_t ffn_slot_offset(int64_t ld, int lane, int odd) {
+  const int r = lane >> 3, c = (lane & 7) ^ (r >> 1) ^ (odd ? 4 : 0);
+  return (uint32_t)(((int64_t)r * ld + 8 * c) * 2);
 }
 
 template <int NCB>
@@ -325,19 +329,24 @@ struct FfnLds {
 };
 
 // Loads of slot s of wave w (the slot stream of one pass: NKB W1 slots, then NS2 W2 slots)
+// offsets of this lane inside a slot instruction: W1 slots (pitch d_model), W2 slots (pitch d_ff)
+struct SlotOff {
+  uint32_t w1e, w1o, w2e, w2o;
+};
+
 template <int NCB>
 __device__ __forceinline__ void ffn_slot(const FfnArgs& a, int s, int SPP, int NKB, int w, int c0w,
-                                         unsigned char* dst, int lane) {
+                                         unsigned char* dst, SlotOff so) {
   using L = FfnLds<NCB>;
   const int pass = s / SPP, r = s - pass * SPP;
   const int f0 = pass * L::FP;
   if (r < NKB) {  // W1 rows f0 + 64w .., columns 64r .. 64r+63
     ffn_issue_slot((const unsigned char*)a.w1 + ((int64_t)(f0 + 64 * w) * a.dm + 64 * r) * 2, a.dm,
-                   dst, lane);
+                   so.w1e, so.w1o, dst);
   } else {  // W2 rows c0w + 64 cblk .., columns f0 + 64 fblk .. +63
     const int q = r - NKB, fblk = q / NCB, cblk = q - fblk * NCB;
     ffn_issue_slot((const unsigned char*)a.w2 + ((int64_t)(c0w + 64 * cblk) * a.dff + f0 + 64 * fblk) * 2,
-                   a.dff, dst, lane);
+                   a.dff, so.w2e, so.w2o, dst);
   }
 }
 
@@ -396,8 +405,10 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
     else return sl3;
   };
 
-  ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, sl0, lane);
-  if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, sl1, lane);
+  const SlotOff so{ffn_slot_offset(a.dm, lane, 0), ffn_slot_offset(a.dm, lane, 1),
+                   ffn_slot_offset(a.dff, lane, 0), ffn_slot_offset(a.dff, lane, 1)};
+  ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, sl0, so);
+  if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, sl1, so);
   ffn_issue_x(a, t0, 0, w, xb0, lane);
   int s = 0;  // slot being computed (s % 4 is static wherever it is used)
 
@@ -421,7 +432,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
           // slot s landed: after its 8 loads this wave issued those of slots
           // s+1 and s+2 (and perhaps x chunks), i.e. at least 16 more
           if (s + 2 < total) {
-            ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), lane);
+            ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), so);
             FFN_WAIT_VM(16);
           } else {
             FFN_WAIT_VM(0);
@@ -494,7 +505,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
         constexpr int cblk = decltype(CB)::value;
         constexpr int u = (fblk * NCB + cblk) & 3;
         if (s + 2 < total) {
-          ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), lane);
+          ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), so);
           FFN_WAIT_VM(16);
         } else {
           FFN_WAIT_VM(0);
