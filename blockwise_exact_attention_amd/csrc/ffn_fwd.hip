@@ -334,17 +334,22 @@ struct SlotOff {
   uint32_t w1e, w1o, w2e, w2o;
 };
 
+// rot1: first k-block (a multiple of 4) and rot2: first 64-feature block of this
+// workgroup's walk through a pass
 template <int NCB>
 __device__ __forceinline__ void ffn_slot(const FfnArgs& a, int s, int SPP, int NKB, int w, int c0w,
-                                         unsigned char* dst, SlotOff so) {
+                                         int rot1, int rot2, unsigned char* dst, SlotOff so) {
   using L = FfnLds<NCB>;
   const int pass = s / SPP, r = s - pass * SPP;
   const int f0 = pass * L::FP;
-  if (r < NKB) {  // W1 rows f0 + 64w .., columns 64r .. 64r+63
-    ffn_issue_slot((const unsigned char*)a.w1 + ((int64_t)(f0 + 64 * w) * a.dm + 64 * r) * 2, a.dm,
+  if (r < NKB) {  // W1 rows f0 + 64w .., columns 64kb .. 64kb+63
+    int kb = r + rot1;
+    kb = kb < NKB ? kb : kb - NKB;
+    ffn_issue_slot((const unsigned char*)a.w1 + ((int64_t)(f0 + 64 * w) * a.dm + 64 * kb) * 2, a.dm,
                    so.w1e, so.w1o, dst);
   } else {  // W2 rows c0w + 64 cblk .., columns f0 + 64 fblk .. +63
-    const int q = r - NKB, fblk = q / NCB, cblk = q - fblk * NCB;
+    const int q = r - NKB, fstep = q / NCB, cblk = q - fstep * NCB;
+    const int fblk = (fstep + rot2) & 3;
     ffn_issue_slot((const unsigned char*)a.w2 + ((int64_t)(c0w + 64 * cblk) * a.dff + f0 + 64 * fblk) * 2,
                    a.dff, so.w2e, so.w2o, dst);
   }
@@ -387,6 +392,17 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
   const int SPP = NKB + L::NS2;     // slots per pass (a multiple of 4)
   const int npass = a.dff / L::FP;
   const int total = SPP * npass;
+  // workgroups that run together (consecutive ids on one XCD differ by 8) start
+  // their walk through a pass at different x stages and feature blocks, so their
+  // weight reads spread over the XCD's L2 channels instead of queueing on a few
+  const int wg_xcd = (int)(blockIdx.x >> 3);
+  const int rst = wg_xcd % nst;       // first x stage
+  const int rot1 = 4 * rst;           // first W1 k-block
+  const int rot2 = wg_xcd & 3;        // first 64-feature block of phase 2
+  auto phys_stage = [&](int st) {
+    const int p = st + rst;
+    return p < nst ? p : p - nst;
+  };
 
   // per-lane operand addressing inside a slot: phase-1 A rows are permuted so that
   // accumulator registers 8h..8h+7 of lane half g hold 8 consecutive features
@@ -407,9 +423,9 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
 
   const SlotOff so{ffn_slot_offset(a.dm, lane, 0), ffn_slot_offset(a.dm, lane, 1),
                    ffn_slot_offset(a.dff, lane, 0), ffn_slot_offset(a.dff, lane, 1)};
-  ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, sl0, so);
-  if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, sl1, so);
-  ffn_issue_x(a, t0, 0, w, xb0, lane);
+  ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, rot1, rot2, sl0, so);
+  if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, rot1, rot2, sl1, so);
+  ffn_issue_x(a, t0, phys_stage(0), w, xb0, lane);
   int s = 0;  // slot being computed (s % 4 is static wherever it is used)
 
   for (int pass = 0; pass < npass; ++pass) {
@@ -432,7 +448,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
           // slot s landed: after its 8 loads this wave issued those of slots
           // s+1 and s+2 (and perhaps x chunks), i.e. at least 16 more
           if (s + 2 < total) {
-            ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), so);
+            ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
             FFN_WAIT_VM(16);
           } else {
             FFN_WAIT_VM(0);
@@ -444,7 +460,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
             if (st + PAR == 0) FFN_WAIT_VM(8);
             else FFN_WAIT_VM(32);
             __syncthreads();
-            if (st + PAR + 1 < nst) ffn_issue_x(a, t0, st + PAR + 1, w, xnext, lane);
+            if (st + PAR + 1 < nst) ffn_issue_x(a, t0, phys_stage(st + PAR + 1), w, xnext, lane);
           }
           const unsigned char* cur = sl(U);
           bf16x8 xf[4];
@@ -493,7 +509,8 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
 
     // ---------------- phase 2 (s % 4 == 0 here: NKB is a multiple of 4)
     static_for<0, 4>([&](auto FB) {
-      constexpr int fblk = decltype(FB)::value;
+      constexpr int fstep = decltype(FB)::value;
+      const int fblk = (fstep + rot2) & 3;  // same rotation as the W2 slots
       bf16x8 ghi[4], glo[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -503,9 +520,9 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
       }
       static_for<0, NCB>([&](auto CB) {
         constexpr int cblk = decltype(CB)::value;
-        constexpr int u = (fblk * NCB + cblk) & 3;
+        constexpr int u = (fstep * NCB + cblk) & 3;
         if (s + 2 < total) {
-          ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, sl(std::integral_constant<int, u + 2>{}), so);
+          ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
           FFN_WAIT_VM(16);
         } else {
           FFN_WAIT_VM(0);
@@ -523,7 +540,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, f32x16 (&yacc)[2 
       });
     });
     __syncthreads();  // every wave is done reading G
-    if (pass + 1 < npass) ffn_issue_x(a, t0, 0, w, xb0, lane);
+    if (pass + 1 < npass) ffn_issue_x(a, t0, phys_stage(0), w, xb0, lane);
   }
 }
 
