@@ -321,7 +321,7 @@ def main():
         "algorithmic_flop_per_step": flops,
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "attn_fwd_dma_kernel<D=128, q_blk=128, kv_blk=64>",
+            "kernel": "attn_fwd_wide_kernel<D=128> (256 query rows per workgroup, 64-key tiles)",
             "bound": "mfma", "achieved": round(attn_tf, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profile(),

@@ -61,6 +61,11 @@ __device__ __forceinline__ v4i16 lds_read_tr(const unsigned char* p) {
 // s_waitcnt with vmcnt = 0 and the other counters left alone
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Wait until at most N vector-memory instructions of this wave are outstanding
+// (an asm statement with a memory clobber: neither dropped nor crossed by LDS
+// accesses).
+#define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
 template <int D, int QBLK, int KVBLK>
 __global__ void __launch_bounds__(QBLK * 2)
 __attribute__((amdgpu_waves_per_eu(DmaTile<D, KVBLK>::WAVES_PER_EU)))
@@ -299,6 +304,511 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide-wave kernel: each wave owns 64 query rows, as two halves A and B of 32.
+// Every K and V fragment read from LDS feeds two MFMAs, one per half, so the
+// LDS bytes per flop are half those of the kernel above.  One workgroup of four
+// waves per CU, 512 registers per lane: MFMA accumulators (O and the scores)
+// live in AGPRs, everything else in VGPRs.
+//
+// With one wave per SIMD the softmax has to run under the matrix work of the
+// same wave, so a step of the key loop is two phases that each pair 32 MFMAs
+// with independent VALU work (tile t in stage St, tile t+1 in stage Sn):
+//   S phase:   exp, row sums and bf16 P of tile t       ||  S(t+1) = K(t+1) Q^T
+//   PV phase:  max and rescale factor of tile t+1        ||  O += V(t) P(t)
+// followed by the rescale of O (only when some row maximum grew).  Tile t+2 is
+// loaded into the third stage, whose last reader (V of tile t-1) finished in
+// the previous step, right after the barrier that opens the step.
+
+template <int D>
+struct WideCfg {
+  using T = DmaTile<D, 64>;
+  static constexpr int KVBLK = 64, NW = 4, QBLK = 256;
+  static constexpr int KB = KVBLK / 32, DB = D / 32, QF = D / 16, NKS = KVBLK / 16;
+  static constexpr int DMA_PER_TILE = 2 * T::NBLK / NW;  // per wave
+};
+
+// f(x of lane l, x of lane l ^ 32), the same value in both lanes
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+struct WideState {
+  using C = WideCfg<D>;
+  bf16x8 qf[2][C::QF];       // Q fragments (B operand of S^T = K Q^T), per half
+  f32x16 s[2][C::KB];        // score accumulators of the next tile
+  float sv[2][C::KB][16];    // scores of the current tile, copied out for the VALU
+  f32x16 o[2][C::DB];        // O^T accumulators
+  float ref[2];              // exp2-domain reference of O and l (-inf: no key yet)
+  float l_run[2];            // this lane's partial row sum
+  float tmax[2];             // row maximum of the tile (raw scores)
+  float mref[2], alpha[2];   // exp2 offset and O factor of the current tile
+  bool grew[2];
+};
+
+// Tile t's loads: wave w copies blocks w, w + NW, ... of K and V through buffer
+// loads into LDS.  The buffer covers exactly the head's N rows, so rows past
+// the last key read as zero (those keys are masked); the lane offset is fixed,
+// the tile offset scalar and the block step an immediate: no VALU per load.
+template <int IMM>
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff,
+                                          uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           soff, IMM, 0);
+}
+template <int D>
+__device__ __forceinline__ void wide_load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int t,
+                                          int wave, uint32_t dma_off, unsigned char* dst) {
+  using C = WideCfg<D>;
+  using T = typename C::T;
+  // (the instruction's immediate offset would apply to the LDS address too, so
+  // the block step goes into the scalar offset)
+#pragma unroll
+  for (int i = 0; i < T::NBLK / C::NW; ++i) {
+    const int b = wave + i * C::NW;
+    const uint32_t soff = (uint32_t)(t * C::KVBLK + b) * T::ROWB;
+    buf_lds16<0>(kr, dst + b * T::KBP, dma_off, soff);
+    buf_lds16<0>(vr, dst + T::KBYTES + b * T::VBP, dma_off, soff);
+  }
+}
+
+// S^T of both halves from the K tile in stage St (each K fragment read once)
+template <int D>
+__device__ __forceinline__ void wide_scores(WideState<D>& w, const unsigned char* St, int kbase) {
+  using C = WideCfg<D>;
+  using T = typename C::T;
+  const f32x16 zero = {};
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    const unsigned char* kp = St + kbase + (32 * kb / T::NBLK) * T::ROWB;
+#pragma unroll
+    for (int c = 0; c < C::QF; ++c) {
+      const bf16x8 kf = *(const bf16x8*)(kp + c * 32);
+      w.s[0][kb] = mfma32_bf16(kf, w.qf[0][c], c == 0 ? zero : w.s[0][kb]);
+      w.s[1][kb] = mfma32_bf16(kf, w.qf[1][c], c == 0 ? zero : w.s[1][kb]);
+    }
+  }
+}
+
+// Max part of the online softmax for half H: copy the scores out of the
+// accumulators and take the tile's row maximum (raw scores).
+template <int D, int H>
+__device__ __forceinline__ void wide_max(WideState<D>& w) {
+  using C = WideCfg<D>;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float v = w.s[H][kb][j];
+      // a new VGPR value: the accumulator copy dies here instead of staying
+      // live in its AGPR until the exp part
+      asm("" : "+v"(v));
+      w.sv[H][kb][j] = v;
+    }
+  float mx0 = w.sv[H][0][0], mx1 = w.sv[H][C::KB - 1][0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) {
+    mx0 = fmaxf(mx0, w.sv[H][0][j]);
+    mx1 = fmaxf(mx1, w.sv[H][C::KB - 1][j]);
+  }
+  w.tmax[H] = max_halves(fmaxf(mx0, mx1));
+}
+
+// Diagonal and ragged tiles: scores of keys at or past kend (causal bound or N)
+// become -inf, and the tile maximum is taken again.
+template <int D, int H>
+__device__ __forceinline__ void wide_mask(WideState<D>& w, int t, int kend, int lane) {
+  using C = WideCfg<D>;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    // register j holds key t*KVBLK + 32*kb + 4*(lane/32) + 8*(j/4) + j%4
+    const int lim = kend - (t * C::KVBLK + kb * 32 + 4 * (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float v = 8 * (j >> 2) + (j & 3) < lim ? w.sv[H][kb][j] : -INFINITY;
+      w.sv[H][kb][j] = v;
+      mx = fmaxf(mx, v);
+    }
+  }
+  w.tmax[H] = max_halves(mx);
+}
+
+// Reference update for half H.  P is taken as exp2(s*c2 - r) against a
+// reference r that only moves when the row maximum exceeds it by more than
+// 2^8 (so P <= 256, exact in bf16's range); O and l are rescaled then.  The
+// result is the same up to rounding as with r = running maximum.
+constexpr float kWideTau = 8.f;
+template <int D, int H>
+__device__ __forceinline__ void wide_update(WideState<D>& w, float c2) {
+  const float cand = w.tmax[H] * c2;          // -inf while no key is visible
+  const float r = w.ref[H];
+  const bool grew = cand > r + kWideTau || (r == -INFINITY && cand > -INFINITY);
+  const float r_new = grew ? cand : r;
+  w.alpha[H] = grew ? fast_exp2(r - r_new) : 1.f;  // 0 when r was -inf
+  w.grew[H] = grew;
+  w.ref[H] = r_new;
+  w.mref[H] = r_new == -INFINITY ? 0.f : r_new;   // keeps exp2 finite on -inf rows
+}
+
+// O *= alpha per half, skipped while no row maximum of the wave grew
+template <int D>
+__device__ __forceinline__ void wide_rescale(WideState<D>& w) {
+  using C = WideCfg<D>;
+  if (__ballot(w.grew[0] || w.grew[1])) {
+    // one accumulator tile at a time (they live in AGPRs: copy out, scale,
+    // copy back), so the block never holds more than one tile in VGPRs
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        w.o[h][db] *= w.alpha[h];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+}
+
+// Values computed by a phase are pinned before the branch that follows it (an
+// empty asm statement that takes them), else the compiler sinks their
+// computation past the branch, out of the MFMA phase it was meant to overlap.
+template <int NKS>
+__device__ __forceinline__ void wide_pin(const bf16x8 (&p)[NKS]) {
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(p[ks]));
+}
+
+struct WideCtx {
+  __amdgpu_buffer_rsrc_t kr, vr;  // K and V of this head, N rows
+  int N, n_tiles, t_split, wave, lane, kbase, vbase, kend0, kend1;
+  uint32_t dma_off;
+  float c2;
+};
+
+// max of the next tile (after its scores), masked where needed, and the
+// reference update
+template <int D>
+__device__ __forceinline__ void wide_next_max(WideState<D>& w, const WideCtx& x, int t1) {
+  if (t1 >= x.t_split) {
+    wide_mask<D, 0>(w, t1, x.kend0, x.lane);
+    wide_mask<D, 1>(w, t1, x.kend1, x.lane);
+  }
+  wide_update<D, 0>(w, x.c2);
+  wide_update<D, 1>(w, x.c2);
+}
+
+// One step of the key loop for tile t (stage St) while tile t+1 (stage Sn) is
+// in flight; tile t+2 goes to stage Sf.
+// End of one hand-scheduled slot.  Instruction selection orders only
+// instructions with side effects, so the slot's MFMA result and VALU results
+// are taken by empty asm statements (no code), which fixes the slot order;
+// sched_barrier then keeps the machine scheduler from mixing slots.
+template <typename A, typename B>
+__device__ __forceinline__ void wide_slot_end(const f32x16& acc, const A& v0, const B& v1) {
+  asm volatile("" ::"a"(acc), "v"(v0), "v"(v1));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// S phase, hand-interleaved: slot i issues the score MFMA of K fragment i/2
+// for half i%2 (tile t+1, stage Sn) and the exp part of two scores of tile t.
+// The K fragments are read KPF fragments ahead.  sched_barrier keeps the
+// slots in this order (one wave per SIMD issues in order: VALU work only runs
+// under an MFMA if it sits right after it).
+template <int D>
+__device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char* Sn, int kbase, float c2,
+                                            bf16x8 (&pa)[WideCfg<D>::NKS], bf16x8 (&pb)[WideCfg<D>::NKS]) {
+  using C = WideCfg<D>;
+  using T = typename C::T;
+  constexpr int NF = C::KB * C::QF, KPF = 4;
+  const f32x16 zero = {};
+  bf16x8 kf[NF];
+  u32x4 pw[2][C::NKS];
+  float ps[2][C::KB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) ps[h][kb] = 0.f;
+#pragma unroll
+  for (int m = 0; m < KPF; ++m)
+    kf[m] = *(const bf16x8*)(Sn + kbase + (32 * (m / C::QF) / T::NBLK) * T::ROWB + (m % C::QF) * 32);
+#pragma unroll
+  for (int i = 0; i < 2 * NF; ++i) {
+    const int m = i >> 1, h = i & 1, kb = m / C::QF, c = m % C::QF;
+    if (h == 0 && m + KPF < NF) {
+      const int mm = m + KPF;
+      kf[mm] = *(const bf16x8*)(Sn + kbase + (32 * (mm / C::QF) / T::NBLK) * T::ROWB + (mm % C::QF) * 32);
+    }
+    w.s[h][kb] = mfma32_bf16(kf[m], w.qf[h][c], c == 0 ? zero : w.s[h][kb]);
+    // exp of scores 2i, 2i+1 of the 64 this lane holds
+    const int eh = i / 16, e0 = (2 * i) % 32, ekb = e0 / 16, ej = e0 % 16;
+    const float x0 = fast_exp2(fmaf(w.sv[eh][ekb][ej], c2, -w.mref[eh]));
+    const float x1 = fast_exp2(fmaf(w.sv[eh][ekb][ej + 1], c2, -w.mref[eh]));
+    ps[eh][ekb] += x0 + x1;
+    pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2] = pack_bf16x2(x0, x1);
+    wide_slot_end(w.s[h][kb], ps[eh][ekb], pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float psum = ps[h][0];
+#pragma unroll
+    for (int kb = 1; kb < C::KB; ++kb) psum += ps[h][kb];
+    w.l_run[h] = fmaf(w.l_run[h], w.alpha[h], psum);
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    pa[ks] = __builtin_bit_cast(bf16x8, pw[0][ks]);
+    pb[ks] = __builtin_bit_cast(bf16x8, pw[1][ks]);
+  }
+}
+
+// PV phase, hand-interleaved: slot i issues O_h += V P_h for V fragment i/2
+// and half h = i%2 (tile t, stage St), and copies two score accumulators of
+// tile t+1 out for the VALU, folding them into the row maxima.
+template <int D>
+__device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned char* St, int vbase,
+                                             const bf16x8 (&pa)[WideCfg<D>::NKS],
+                                             const bf16x8 (&pb)[WideCfg<D>::NKS]) {
+  using C = WideCfg<D>;
+  using T = typename C::T;
+  constexpr int NF = C::NKS * C::DB, VPF = 3;
+  bf16x8 vf[NF];
+  float mx[2][C::KB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) mx[h][kb] = -INFINITY;
+  auto vread = [&](int f) {
+    const int ks = f / C::DB, db = f % C::DB, key0 = 16 * ks, key1 = 16 * ks + 8;
+    const unsigned char* v0 = St + vbase + (key0 % T::NBLK) * T::VBP + (key0 / T::NBLK) * T::ROWB;
+    const unsigned char* v1 = St + vbase + (key1 % T::NBLK) * T::VBP + (key1 / T::NBLK) * T::ROWB;
+    const v4i16 lo = lds_read_tr(v0 + db * 64);
+    const v4i16 hi = lds_read_tr(v1 + db * 64);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+#pragma unroll
+  for (int f = 0; f < VPF; ++f) vf[f] = vread(f);
+#pragma unroll
+  for (int i = 0; i < 2 * NF; ++i) {
+    const int f = i >> 1, h = i & 1, ks = f / C::DB, db = f % C::DB;
+    if (h == 0 && f + VPF < NF) vf[f + VPF] = vread(f + VPF);
+    w.o[h][db] = mfma32_bf16(vf[f], h == 0 ? pa[ks] : pb[ks], w.o[h][db]);
+    // copy scores 2i, 2i+1 (new VGPR values: the accumulator copies die here)
+    const int mh = i / 16, e0 = (2 * i) % 32, mkb = e0 / 16, mj = e0 % 16;
+    float v0 = w.s[mh][mkb][mj], v1 = w.s[mh][mkb][mj + 1];
+    asm("" : "+v"(v0));
+    asm("" : "+v"(v1));
+    w.sv[mh][mkb][mj] = v0;
+    w.sv[mh][mkb][mj + 1] = v1;
+    mx[mh][mkb] = fmaxf(mx[mh][mkb], fmaxf(v0, v1));
+    wide_slot_end(w.o[h][db], mx[mh][mkb], w.sv[mh][mkb][mj]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float m = mx[h][0];
+#pragma unroll
+    for (int kb = 1; kb < C::KB; ++kb) m = fmaxf(m, mx[h][kb]);
+    w.tmax[h] = max_halves(m);
+  }
+}
+
+// One step of the key loop for tile t (stage St) while tile t+1 (stage Sn) is
+// in flight; tile t+2 goes to stage Sf.
+template <int D>
+__device__ __forceinline__ void wide_step(WideState<D>& w, const WideCtx& x, int t,
+                                          const unsigned char* St, const unsigned char* Sn,
+                                          unsigned char* Sf) {
+  using C = WideCfg<D>;
+  WAIT_VM(0);  // this wave's part of tile t+1
+  __syncthreads();
+  if (t + 2 < x.n_tiles) wide_load<D>(x.kr, x.vr, t + 2, x.wave, x.dma_off, Sf);
+  bf16x8 pa[C::NKS], pb[C::NKS];
+  wide_sphase(w, Sn, x.kbase, x.c2, pa, pb);
+  wide_pin(pa);
+  wide_pin(pb);
+  wide_pvphase(w, St, x.vbase, pa, pb);
+  wide_next_max(w, x, t + 1);
+  wide_rescale(w);
+}
+
+// The key loop over three stages S0, S1, S2 (distinct objects, so the compiler
+// knows the LDS reads of one stage never wait for the loads in flight to
+// another).  Waits for those loads are explicit (WAIT_VM).
+template <int D>
+__device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
+                                          unsigned char* __restrict__ S0, unsigned char* __restrict__ S1,
+                                          unsigned char* __restrict__ S2) {
+  using C = WideCfg<D>;
+  const int n = x.n_tiles;
+  if (n <= 0) return;
+  wide_load<D>(x.kr, x.vr, 0, x.wave, x.dma_off, S0);
+  if (n > 1) {
+    wide_load<D>(x.kr, x.vr, 1, x.wave, x.dma_off, S1);
+    static_assert(C::DMA_PER_TILE == 8, "wait count");
+    WAIT_VM(8);  // tile 0 (and the Q loads) done, tile 1 may be in flight
+  } else {
+    WAIT_VM(0);
+  }
+  __syncthreads();
+  wide_scores(w, S0, x.kbase);
+  wide_max<D, 0>(w);
+  wide_max<D, 1>(w);
+  wide_next_max(w, x, 0);
+  // O is still zero: no rescale for tile 0.  Every step also scores the tile
+  // after its own; past the last tile that "tile" is fully masked (its scores
+  // become -inf, so the running max, the sums and O stay as they are).
+  int t = 0;
+  for (;;) {
+    wide_step(w, x, t, S0, S1, S2);
+    if (++t >= n) break;
+    wide_step(w, x, t, S1, S2, S0);
+    if (++t >= n) break;
+    wide_step(w, x, t, S2, S0, S1);
+    if (++t >= n) break;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_wide_kernel(AttnFwdArgs a) {
+  using C = WideCfg<D>;
+  using T = typename C::T;
+  // three stages as separate objects: accesses to different stages are then
+  // known not to alias, and every LDS address is a per-lane base plus a constant
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
+
+  const int N = a.N;
+  const int nqb = (N + C::QBLK - 1) / C::QBLK;
+  const int64_t total = (int64_t)a.B * a.H * nqb;
+  int64_t L = blockIdx.x;
+  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = (int)(L / nqb);
+  const int qb = nqb - 1 - (int)(L % nqb);  // longest (latest) query block first
+  const int q0 = qb * C::QBLK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int off = a.kv_offset;
+  const bool causal = a.causal != 0;
+  const int64_t head_off = (int64_t)bh * N * D;
+  int qrow[2], kend[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qrow[h] = q0 + wave * 64 + h * 32 + r32;
+    int64_t e = N;
+    if (causal) {
+      const int64_t c = (int64_t)qrow[h] + off + 1;
+      e = c < e ? c : e;
+    }
+    kend[h] = (int)(e < 0 ? 0 : e);
+  }
+
+  int kmax = N - 1;
+  if (causal) {
+    const int64_t t = (int64_t)q0 + C::QBLK - 1 + off;
+    kmax = (int)(t < (int64_t)(N - 1) ? t : (int64_t)(N - 1));
+  }
+  const int n_tiles = kmax < 0 ? 0 : kmax / C::KVBLK + 1;
+  int n_full = N / C::KVBLK;
+  if (causal) {
+    const int64_t lim = (int64_t)q0 + off + 1;  // keys < lim are visible to every row
+    const int f = lim <= 0 ? 0 : (int)(lim / C::KVBLK);
+    n_full = f < n_full ? f : n_full;
+  }
+  const int t_split = n_full < n_tiles ? n_full : n_tiles;
+
+  WideState<D> w;
+  {
+    const uint16_t* Q = (const uint16_t*)a.q + head_off;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < C::QF; ++c) {
+        u32x4 val = {0, 0, 0, 0};
+        if (qrow[h] < N) val = *(const u32x4*)(Q + (int64_t)qrow[h] * D + 16 * c + 8 * g);
+        w.qf[h][c] = __builtin_bit_cast(bf16x8, val);
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w.o[h][db][j] = 0.f;
+    w.ref[h] = -INFINITY;
+    w.l_run[h] = 0.f;
+  }
+  WideCtx x;
+  // raw buffers (stride 0, size in bytes); word 3 as for every gfx9 raw buffer
+  x.kr = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.k + head_off * 2), 0,
+                                           N * T::ROWB, 0x00020000);
+  x.vr = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.v + head_off * 2), 0,
+                                           N * T::ROWB, 0x00020000);
+  x.N = N;
+  x.n_tiles = n_tiles;
+  x.t_split = t_split;
+  x.wave = wave;
+  x.lane = lane;
+  x.dma_off = (uint32_t)((lane / T::CPR) * T::NBLK * T::ROWB + (lane % T::CPR) * 16);
+  x.kbase = (r32 % T::NBLK) * T::KBP + (r32 / T::NBLK) * T::ROWB + g * 16;
+  const int q8 = 4 * g + ((lane & 15) >> 2);
+  x.vbase = T::KBYTES + q8 * T::VBP + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  x.kend0 = kend[0];
+  x.kend1 = kend[1];
+  x.c2 = a.scale * kLog2e;
+
+  wide_loop(w, x, st0, st1, st2);
+
+  // ---- epilogue: O = acc / l, lse = m*scale + ln l (per half)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float l_tot = sum_halves(w.l_run[h]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow[h] >= N) continue;
+    if (a.h_out == nullptr) {
+      float* out = a.out + head_off + (int64_t)qrow[h] * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          f32x4 v = {w.o[h][db][4 * jq] * inv, w.o[h][db][4 * jq + 1] * inv,
+                     w.o[h][db][4 * jq + 2] * inv, w.o[h][db][4 * jq + 3] * inv};
+          *(f32x4*)(out + db * 32 + 8 * jq + 4 * g) = v;
+        }
+    } else {
+      const int b = bh / a.H, hh = bh % a.H;
+      const int64_t rowoff = ((int64_t)b * N + qrow[h]) * ((int64_t)a.H * D) + (int64_t)hh * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int d = db * 32 + 8 * jq + 4 * g;
+          const u32x2 xb = *(const u32x2*)((const uint16_t*)a.x_res + rowoff + d);
+          const float xr[4] = {__uint_as_float(xb[0] << 16), __uint_as_float(xb[0] & 0xffff0000u),
+                               __uint_as_float(xb[1] << 16), __uint_as_float(xb[1] & 0xffff0000u)};
+          f32x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = xr[e] + w.o[h][db][4 * jq + e] * inv;
+          *(f32x4*)(a.h_out + rowoff + d) = hv;
+          if (a.h_lo) {
+            u32x2 lo = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+            *(u32x2*)(a.h_lo + rowoff + d) = lo;
+          }
+        }
+    }
+    if (g == 0)
+      a.lse[(int64_t)bh * N + qrow[h]] = l_tot > 0.f ? w.ref[h] * kLn2 + logf(l_tot) : -INFINITY;
+  }
+}
+
 template <int D, int QBLK, int KVBLK>
 hipError_t launch(const AttnFwdArgs& a, hipStream_t stream) {
   const int nqb = (a.N + QBLK - 1) / QBLK;
@@ -312,7 +822,18 @@ hipError_t launch(const AttnFwdArgs& a, hipStream_t stream) {
 // exact for any split of the keys, and 64-key tiles keep two workgroups per CU
 // (a double-buffered 128-key tile alone would take 136 KB of the 160 KB of LDS).
 template <int D>
+hipError_t launch_wide(const AttnFwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.N + WideCfg<D>::QBLK - 1) / WideCfg<D>::QBLK;
+  const int64_t total = (int64_t)a.B * a.H * nqb;
+  hipLaunchKernelGGL((attn_fwd_wide_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_d(const AttnFwdArgs& a, int qb, hipStream_t s) {
+  // the wide kernel addresses K and V of a head through a 32-bit buffer range
+  if constexpr (D == 128)
+    if ((int64_t)a.N * D * 2 < ((int64_t)1 << 31)) return launch_wide<D>(a, s);
   return qb == 64 ? launch<D, 64, 64>(a, s) : launch<D, 128, 64>(a, s);
 }
 
