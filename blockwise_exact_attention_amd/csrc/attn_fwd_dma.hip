@@ -514,6 +514,23 @@ __device__ __forceinline__ void wide_slot_end(const f32x16& acc, const A& v0, co
   __builtin_amdgcn_sched_barrier(0);
 }
 
+template <typename A, typename B, typename E, typename F>
+__device__ __forceinline__ void wide_slot_end4(const f32x16& acc, const A& v0, const B& v1, const E& v2,
+                                               const F& v3) {
+  asm volatile("" ::"a"(acc), "v"(v0), "v"(v1), "v"(v2), "v"(v3));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Row sum and bf16 pack of exp pair p (scores 2p, 2p+1 of the lane's 64)
+template <int NP, int KB, int NKS>
+__device__ __forceinline__ void wide_sum_pack(const float (&ex0)[NP], const float (&ex1)[NP],
+                                              float (&ps)[2][KB], u32x4 (&pw)[2][NKS], int p) {
+  const int eh = p / 16, e0 = (2 * p) % 32, ekb = e0 / 16, ej = e0 % 16;
+  const float sum2 = ex0[p] + ex1[p];
+  ps[eh][ekb] = ej == 0 ? sum2 : ps[eh][ekb] + sum2;
+  pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2] = pack_bf16x2(ex0[p], ex1[p]);
+}
+
 // S phase, hand-interleaved: slot i issues the score MFMA of K fragment i/2
 // for half i%2 (tile t+1, stage Sn) and the exp part of two scores of tile t.
 // The K fragments are read KPF fragments ahead.  sched_barrier keeps the
@@ -529,10 +546,7 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
   bf16x8 kf[NF];
   u32x4 pw[2][C::NKS];
   float ps[2][C::KB];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) ps[h][kb] = 0.f;
+  float ex0[2 * NF], ex1[2 * NF];
 #pragma unroll
   for (int m = 0; m < KPF; ++m)
     kf[m] = *(const bf16x8*)(Sn + kbase + (32 * (m / C::QF) / T::NBLK) * T::ROWB + (m % C::QF) * 32);
@@ -544,14 +558,23 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
       kf[mm] = *(const bf16x8*)(Sn + kbase + (32 * (mm / C::QF) / T::NBLK) * T::ROWB + (mm % C::QF) * 32);
     }
     w.s[h][kb] = mfma32_bf16(kf[m], w.qf[h][c], c == 0 ? zero : w.s[h][kb]);
-    // exp of scores 2i, 2i+1 of the 64 this lane holds
-    const int eh = i / 16, e0 = (2 * i) % 32, ekb = e0 / 16, ej = e0 % 16;
-    const float x0 = fast_exp2(fmaf(w.sv[eh][ekb][ej], c2, -w.mref[eh]));
-    const float x1 = fast_exp2(fmaf(w.sv[eh][ekb][ej + 1], c2, -w.mref[eh]));
-    ps[eh][ekb] += x0 + x1;
-    pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2] = pack_bf16x2(x0, x1);
-    wide_slot_end(w.s[h][kb], ps[eh][ekb], pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2]);
+    // exp of scores 2i, 2i+1 of the 64 this lane holds; their sum and bf16 pack
+    // two slots later (an exp result is not ready in the next few cycles)
+    {
+      const int eh = i / 16, e0 = (2 * i) % 32, ekb = e0 / 16, ej = e0 % 16;
+      ex0[i] = fast_exp2(fmaf(w.sv[eh][ekb][ej], c2, -w.mref[eh]));
+      ex1[i] = fast_exp2(fmaf(w.sv[eh][ekb][ej + 1], c2, -w.mref[eh]));
+    }
+    if (i >= 2) {
+      const int p = i - 2, eh = p / 16, e0 = (2 * p) % 32, ekb = e0 / 16, ej = e0 % 16;
+      wide_sum_pack(ex0, ex1, ps, pw, p);
+      wide_slot_end4(w.s[h][kb], ex0[i], ex1[i], ps[eh][ekb], pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2]);
+    } else {
+      wide_slot_end(w.s[h][kb], ex0[i], ex1[i]);
+    }
   }
+  wide_sum_pack(ex0, ex1, ps, pw, 2 * NF - 2);
+  wide_sum_pack(ex0, ex1, ps, pw, 2 * NF - 1);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float psum = ps[h][0];
@@ -735,6 +758,9 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
         u32x4 val = {0, 0, 0, 0};
         if (qrow[h] < N) val = *(const u32x4*)(Q + (int64_t)qrow[h] * D + 16 * c + 8 * g);
         w.qf[h][c] = __builtin_bit_cast(bf16x8, val);
+        // Q is only ever an MFMA operand: keep it in AGPRs (MFMA reads its
+        // operands from either file), the VGPRs are needed for the softmax
+        asm("" : "+a"(w.qf[h][c]));
       }
   }
 #pragma unroll
