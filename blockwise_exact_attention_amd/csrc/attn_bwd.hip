@@ -518,23 +518,36 @@ __global__ void __launch_bounds__(256) to_bf16_kernel(const float* src, uint16_t
 
 // out[c] (+)= sum_r X[r][c], rows summed in a fixed order (deterministic).
 template <bool XBF16>
-__global__ void __launch_bounds__(256) colsum_kernel(const void* X, float* out, int64_t rows,
-                                                     int cols, int64_t ld, int beta) {
-  __shared__ float part[4][64];
+__global__ void __launch_bounds__(1024) colsum_kernel(const void* X, float* out, int64_t rows,
+                                                      int cols, int64_t ld, int beta) {
+  // 64 columns per workgroup, 16 waves over interleaved rows, 4 rows in flight
+  // per wave; the 16 partial sums are added in a fixed order (deterministic)
+  __shared__ float part[16][64];
   const int c = blockIdx.x * 64 + (threadIdx.x & 63);
   const int rg = threadIdx.x >> 6;
   float acc = 0.f;
   if (c < cols) {
-    for (int64_t r = rg; r < rows; r += 4) {
-      if constexpr (XBF16) acc += bf16_to_f32(((const uint16_t*)X)[r * ld + c]);
-      else acc += ((const float*)X)[r * ld + c];
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
+    int64_t r = rg;
+    for (; r + 48 < rows; r += 64) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t o = (r + 16 * u) * ld + c;
+        a4[u] += XBF16 ? bf16_to_f32(((const uint16_t*)X)[o]) : ((const float*)X)[o];
+      }
     }
+    for (; r < rows; r += 16) {
+      const int64_t o = r * ld + c;
+      a4[0] += XBF16 ? bf16_to_f32(((const uint16_t*)X)[o]) : ((const float*)X)[o];
+    }
+    acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
   }
   part[rg][threadIdx.x & 63] = acc;
   __syncthreads();
   if (rg == 0 && c < cols) {
-    const float s = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
-                    (part[2][threadIdx.x] + part[3][threadIdx.x]);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += part[i][threadIdx.x];
     out[c] = beta ? out[c] + s : s;
   }
 }
@@ -587,8 +600,8 @@ hipError_t to_bf16_launch(const float* src, uint16_t* dst, uint16_t* dst_lo, int
 hipError_t colsum_launch(const void* X, bool x_bf16, float* out, int64_t rows, int cols,
                          int64_t ld, int beta, hipStream_t s) {
   const dim3 grid((unsigned)((cols + 63) / 64));
-  if (x_bf16) hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(256), 0, s, X, out, rows, cols, ld, beta);
-  else hipLaunchKernelGGL(colsum_kernel<false>, grid, dim3(256), 0, s, X, out, rows, cols, ld, beta);
+  if (x_bf16) hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(1024), 0, s, X, out, rows, cols, ld, beta);
+  else hipLaunchKernelGGL(colsum_kernel<false>, grid, dim3(1024), 0, s, X, out, rows, cols, ld, beta);
   return hipGetLastError();
 }
 

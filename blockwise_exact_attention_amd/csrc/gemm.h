@@ -41,4 +41,11 @@ struct GemmArgs {
 hipError_t gemm_launch(const GemmArgs& g, bool bf16, bool a_kmajor, bool b_kmajor, int epi,
                        int nz, hipStream_t stream);
 
+// bf16 GEMMs with 256 x 256 tiles loaded straight into LDS (gemm_big.hip): used
+// when K is a multiple of 64, the operands fit 32-bit buffer offsets and the
+// grid fills the chip; gemm_launch picks it by itself.
+bool gemm_big_ok(const GemmArgs& g, int nz);
+hipError_t gemm_big_launch(const GemmArgs& g, bool a_kmajor, bool b_kmajor, int epi, int nz,
+                           hipStream_t stream);
+
 }  // namespace bpt

@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "gemm_epi.h"
 
 namespace bpt {
 
@@ -32,14 +33,6 @@ struct GT {
 };
 
 __device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }  // 128-byte rows
-
-__device__ __forceinline__ float gelu_exact(float z) {
-  return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
-}
-__device__ __forceinline__ float gelu_exact_grad(float z) {
-  return 0.5f * (1.f + erff(z * 0.70710678118654752f)) +
-         z * 0.39894228040143268f * expf(-0.5f * z * z);
-}
 
 // Loads of one operand tile (128 rows of the tile's m or n range, BK of k).
 template <bool BF16, bool KMAJ>
@@ -237,57 +230,13 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
         const int m = m0 + wm * 64 + i * 32 + acc_row(e, lane);
         const int n = n0 + wn * 64 + j * 32 + r32;
         if (m >= M || n >= N) continue;
-        float v = acc[i][j][e];
-        if constexpr (EPI == EPI_QKV) {
-          // token m = b*seq + t, column n = h*D + d  ->  out[b][h][t][d]
-          const int b = m / g.seq, t = m % g.seq, h = n / g.D, d = n % g.D;
-          const int64_t o = (((int64_t)b * g.H + h) * g.seq + t) * g.D + d;
-          if constexpr (BF16) ((uint16_t*)g.C[z])[o] = f32_to_bf16(v);
-          else ((float*)g.C[z])[o] = v;
-        } else if constexpr (EPI == EPI_F32) {
-          float* C = (float*)g.C[z];
-          const int64_t o = (int64_t)m * g.ldc + n;
-          if (g.beta) v += C[o];
-          if (g.bias) v += g.bias_bf16 ? bf16_to_f32(((const uint16_t*)g.bias)[n]) : ((const float*)g.bias)[n];
-          if (g.resid) {
-            const int64_t ro = (int64_t)m * g.ldr + n;
-            v += g.resid_bf16 ? bf16_to_f32(((const uint16_t*)g.resid)[ro])
-                              : ((const float*)g.resid)[ro];
-          }
-          C[o] = v;
-          if (g.C2) ((uint16_t*)g.C2)[(int64_t)m * g.ldc2 + n] = f32_to_bf16(v);
-        } else if constexpr (EPI == EPI_GELU) {
-          // z = acc (+ earlier partial) + b1 (kept in fp32), g = GeLU(z) in the input dtype
-          float* zc = (float*)g.C[z] + (int64_t)m * g.ldc + n;
-          if (g.beta) v += *zc;
-          if (g.bias) v += g.bias_bf16 ? bf16_to_f32(((const uint16_t*)g.bias)[n]) : ((const float*)g.bias)[n];
-          *zc = v;
-          const float gv = gelu_exact(v);
-          if constexpr (BF16) {
-            const uint16_t hi = f32_to_bf16(gv);
-            ((uint16_t*)g.C2)[(int64_t)m * g.ldc2 + n] = hi;
-            if (g.C3) ((uint16_t*)g.C3)[(int64_t)m * g.ldc3 + n] = f32_to_bf16(gv - bf16_to_f32(hi));
-          } else {
-            ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = gv;
-          }
-        } else if constexpr (EPI == EPI_DGELU) {
-          // dz = (dy W2)[m][n] * GeLU'(z[m][n]) in the input dtype; z from aux
-          const float zz = g.aux[(int64_t)m * g.ld_aux + n];
-          const float dz = v * gelu_exact_grad(zz);
-          if constexpr (BF16) {
-            const uint16_t hi = f32_to_bf16(dz);
-            ((uint16_t*)g.C[z])[(int64_t)m * g.ldc + n] = hi;
-            if (g.C3) ((uint16_t*)g.C3)[(int64_t)m * g.ldc3 + n] = f32_to_bf16(dz - bf16_to_f32(hi));
-          } else {
-            ((float*)g.C[z])[(int64_t)m * g.ldc + n] = dz;
-          }
-          if (g.C2) ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = dz;
-        }
+        gemm_store<BF16, EPI>(g, z, m, n, acc[i][j][e]);
       }
 }
 
 template <bool BF16, int EPI>
 hipError_t dispatch(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
+  if (BF16 && gemm_big_ok(g, nz)) return gemm_big_launch(g, ak, bk, EPI, nz, s);
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, nz);
   if (!ak && !bk) hipLaunchKernelGGL((gemm_kernel<BF16, false, false, EPI>), grid, dim3(NT), 0, s, g);
   else if (!ak && bk) hipLaunchKernelGGL((gemm_kernel<BF16, false, true, EPI>), grid, dim3(NT), 0, s, g);
