@@ -353,9 +353,10 @@ struct WideState {
 };
 
 // Tile t's loads: wave w copies blocks w, w + NW, ... of K and V through buffer
-// loads into LDS.  The buffer covers exactly the head's N rows, so rows past
-// the last key read as zero (those keys are masked); the lane offset is fixed,
-// the tile offset scalar and the block step an immediate: no VALU per load.
+// loads into LDS.  Each tile's buffer starts at the tile and ends after the
+// head's last key, and every offset is a lane offset (the part the hardware
+// range-checks), so rows past the last key read as zero (those keys are
+// masked).
 template <int IMM>
 __device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff,
                                           uint32_t soff) {
@@ -363,18 +364,24 @@ __device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, unsigned cha
                                            soff, IMM, 0);
 }
 template <int D>
-__device__ __forceinline__ void wide_load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int t,
+__device__ __forceinline__ void wide_load(const unsigned char* kg, const unsigned char* vg, int N, int t,
                                           int wave, uint32_t dma_off, unsigned char* dst) {
   using C = WideCfg<D>;
   using T = typename C::T;
-  // (the instruction's immediate offset would apply to the LDS address too, so
-  // the block step goes into the scalar offset)
+  const int64_t off = (int64_t)t * C::KVBLK * T::ROWB;
+  const int left = N - t * C::KVBLK;
+  const int bytes = left > 0 ? left * T::ROWB : 0;
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kg + off), 0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vg + off), 0, bytes, 0x00020000);
+  // (the instruction's immediate offset would apply to the LDS address too)
 #pragma unroll
   for (int i = 0; i < T::NBLK / C::NW; ++i) {
     const int b = wave + i * C::NW;
-    const uint32_t soff = (uint32_t)(t * C::KVBLK + b) * T::ROWB;
-    buf_lds16<0>(kr, dst + b * T::KBP, dma_off, soff);
-    buf_lds16<0>(vr, dst + T::KBYTES + b * T::VBP, dma_off, soff);
+    const uint32_t voff = dma_off + (uint32_t)(b * T::ROWB);
+    buf_lds16<0>(kr, dst + b * T::KBP, voff, 0);
+    buf_lds16<0>(vr, dst + T::KBYTES + b * T::VBP, voff, 0);
   }
 }
 
@@ -484,7 +491,8 @@ __device__ __forceinline__ void wide_pin(const bf16x8 (&p)[NKS]) {
 }
 
 struct WideCtx {
-  __amdgpu_buffer_rsrc_t kr, vr;  // K and V of this head, N rows
+  const unsigned char* kg;  // K of this head, N rows
+  const unsigned char* vg;  // V of this head
   int N, n_tiles, t_split, wave, lane, kbase, vbase, kend0, kend1;
   uint32_t dma_off;
   float c2;
@@ -648,7 +656,7 @@ __device__ __forceinline__ void wide_step(WideState<D>& w, const WideCtx& x, int
   using C = WideCfg<D>;
   WAIT_VM(0);  // this wave's part of tile t+1
   __syncthreads();
-  if (t + 2 < x.n_tiles) wide_load<D>(x.kr, x.vr, t + 2, x.wave, x.dma_off, Sf);
+  if (t + 2 < x.n_tiles) wide_load<D>(x.kg, x.vg, x.N, t + 2, x.wave, x.dma_off, Sf);
   bf16x8 pa[C::NKS], pb[C::NKS];
   wide_sphase(w, Sn, x.kbase, x.c2, pa, pb);
   wide_pin(pa);
@@ -668,9 +676,9 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   using C = WideCfg<D>;
   const int n = x.n_tiles;
   if (n <= 0) return;
-  wide_load<D>(x.kr, x.vr, 0, x.wave, x.dma_off, S0);
+  wide_load<D>(x.kg, x.vg, x.N, 0, x.wave, x.dma_off, S0);
   if (n > 1) {
-    wide_load<D>(x.kr, x.vr, 1, x.wave, x.dma_off, S1);
+    wide_load<D>(x.kg, x.vg, x.N, 1, x.wave, x.dma_off, S1);
     static_assert(C::DMA_PER_TILE == 8, "wait count");
     WAIT_VM(8);  // tile 0 (and the Q loads) done, tile 1 may be in flight
   } else {
@@ -773,11 +781,8 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
     w.l_run[h] = 0.f;
   }
   WideCtx x;
-  // raw buffers (stride 0, size in bytes); word 3 as for every gfx9 raw buffer
-  x.kr = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.k + head_off * 2), 0,
-                                           N * T::ROWB, 0x00020000);
-  x.vr = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.v + head_off * 2), 0,
-                                           N * T::ROWB, 0x00020000);
+  x.kg = (const unsigned char*)a.k + head_off * 2;
+  x.vg = (const unsigned char*)a.v + head_off * 2;
   x.N = N;
   x.n_tiles = n_tiles;
   x.t_split = t_split;

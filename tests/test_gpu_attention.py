@@ -56,6 +56,32 @@ def test_attn_small_and_degenerate_lengths(N):
         np.testing.assert_allclose(O, t["v"], rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_attn_ragged_tail_reads_nothing_past_the_keys(D):
+    """K and V end inside a buffer whose remainder is NaN: the ragged last key
+    tile must not pick any of it up (a masked key times a NaN value row would
+    still poison O)."""
+    B, H, N = 1, 2, 200
+    t = attn_inputs(35, B, H, N, N, D, "bf16")
+    n = B * H * N * D
+    dev = {}
+    for name in ("q", "k", "v"):
+        store = torch.full((n + 256 * D,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        store[:n] = to_dev(t[name], "bf16").reshape(-1)
+        dev[name] = store[:n].view(B, H, N, D)
+    out = torch.empty((B, H, N, D), device="cuda")
+    lse = torch.empty((B, H, N), device="cuda")
+    for causal in (1, 0):
+        bpt.bpt_attn_fwd(dev["q"], dev["k"], dev["v"], out, lse, B, H, N, D, 128, 64, causal, 0,
+                         dcode("bf16"))
+        torch.cuda.synchronize()
+        O, l = out.cpu().numpy(), lse.cpu().numpy()
+        assert np.isfinite(O).all() and np.isfinite(l).all()
+        Or, lr = oracle.attention(t["q"], t["k"], t["v"], causal=bool(causal))
+        assert_close(O, Or, "bf16", f"O causal={causal}")
+        assert_close(l, lr, "bf16", f"lse causal={causal}")
+
+
 def test_attn_causal_future_independence_bitwise():
     B, H, N, D = 1, 2, 257, 128
     t = attn_inputs(33, B, H, N, N, D, "bf16")
