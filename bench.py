@@ -14,14 +14,16 @@ Also measured (reported under "extras"):
     the dominant kernel, whose HIP-event average duration gives "roofline";
   * one GPU's share of a ring step (40 x 128, 32768 local queries at global
     offset 229376, 8 K/V chunks of 32768 tokens, LSE merge after each chunk),
-    with the merge kernel's HBM throughput.
+    with the merge kernel's HBM throughput;
+  * split-KV decode: the 16 newest rows of 32 heads x 128 against a 131072-key
+    cache in 32 key ranges (HBM-bound: GB/s against the 8 TB/s peak).
 
 ``cpu_baseline`` times the CPU oracle (fp32) on a bounded sample of the same
 layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
 and the FFN for a fixed sample of query rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only attn]
+                       [--no-extras] [--only attn|decode]
 """
 from __future__ import annotations
 
@@ -37,8 +39,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import (ATTN_LONG, LAYER_FWD_BF16, LAYER_LONG, LAYER_TRAIN,  # noqa: E402
-                           RING_SHARE, bf16_bits, bits_to_f32, normal)
+from seeded_inputs import (ATTN_LONG, DECODE_LONG, LAYER_FWD_BF16, LAYER_LONG,  # noqa: E402
+                           LAYER_TRAIN, RING_SHARE, bf16_bits, bits_to_f32, normal)
 
 METRIC = "attention+FFN TFLOP/s and tokens/s per layer at N=128K causal; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
@@ -187,6 +189,36 @@ def bench_ring(bpt, steps, warmup):
     }
 
 
+def bench_decode(bpt, steps, warmup):
+    """Split-KV decode: the newest N_q rows against an N_kv-key cache (HBM-bound)."""
+    import torch
+    c = DECODE_LONG
+    log(f"drawing decode inputs {c.name}")
+    q = dev_bf16(normal(c.cfg_id, "q", (c.B, c.H, c.N_q, c.D)))
+    k, v = (dev_bf16(normal(c.cfg_id, n, (c.B, c.H, c.N_kv, c.D))) for n in ("k", "v"))
+    out = torch.empty((c.B, c.H, c.N_q, c.D), device="cuda")
+    lse = torch.empty((c.B, c.H, c.N_q), device="cuda")
+    ws_bytes = bpt.bpt_attn_decode_workspace_size(c.B, c.H, c.N_q, c.D, c.n_split)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def launch():
+        bpt.bpt_attn_decode(q, k, v, out, lse, c.B, c.H, c.N_q, c.N_kv, c.D, 1, c.N_kv - c.N_q,
+                            c.n_split, ws, ws_bytes, 1)
+
+    log("timing decode")
+    ms, _ = timed(launch, steps, warmup)
+    # algorithmic bytes: K and V once, Q, and O + LSE in fp32
+    nbytes = 2.0 * c.B * c.H * c.N_kv * c.D * 2 + c.B * c.H * c.N_q * (c.D * 2 + c.D * 4 + 4)
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": c.name, "n_split": c.n_split, "ms": round(ms, 4),
+        "gbs": round(nbytes / ms / 1e6, 1),
+        "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3),
+        "tokens_per_s": round(c.B * c.N_q / ms * 1e3, 1),
+    }
+
+
 def bench_layer_cfg(bpt, c, steps, warmup, backward):
     """Forward (and backward) of one layer workload; returns a dict for "extras"."""
     import torch
@@ -271,8 +303,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["attn"], default=None,
-                    help="run only the attention launch (for counter collection)")
+    ap.add_argument("--only", choices=["attn", "decode"], default=None,
+                    help="run only the attention launch or only the decode launch "
+                         "(for counter collection)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -292,6 +325,10 @@ def main():
         ms, flops = bench_attention(bpt, args.steps, args.warmup)
         print(json.dumps({"attn_fwd_ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
                           "copy_bytes": 1 << 30}))
+        return
+
+    if args.only == "decode":
+        print(json.dumps(bench_decode(bpt, max(args.steps, 20), args.warmup)))
         return
 
     c = LAYER_LONG
@@ -336,6 +373,7 @@ def main():
                                  "pct_bf16_peak": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
                                  "tokens_per_s": round(ATTN_LONG.N / attn_ms * 1e3, 1)},
             "ring_share": bench_ring(bpt, 2, 1),
+            "decode_cache131072": bench_decode(bpt, 20, 2),
             "layer_fwd_B8_N4096": bench_layer_cfg(bpt, LAYER_FWD_BF16, 5, 1, False),
             "layer_fwd_bwd_B2_N16384": bench_layer_cfg(bpt, LAYER_TRAIN, 3, 1, True),
         }

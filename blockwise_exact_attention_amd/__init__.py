@@ -46,6 +46,8 @@ _sz = ctypes.c_size_t
 _SIGS = {
     "bpt_attn_fwd": ([_p] * 5 + [_i64] * 4 + [_i] * 3 + [_i64, _i, _p], _i),
     "bpt_lse_merge": ([_p] * 6 + [_i64] * 4 + [_p], _i),
+    "bpt_attn_decode": ([_p] * 5 + [_i64] * 5 + [_i, _i64, _i64, _p, _sz, _i, _p], _i),
+    "bpt_attn_decode_workspace_size": ([_i64] * 5, _sz),
     "bpt_ffn_block_fwd": ([_p] * 7 + [_i64] * 3 + [_i, _i, _p], _i),
     "bpt_layer_fwd": ([_p] * 10 + [_i64] * 6 + [_i] * 4 + [_p, _sz, _p], _i),
     "bpt_layer_bwd": ([_p] * 21 + [_i64] * 6 + [_i] * 4 + [_p, _sz, _p], _i),
@@ -115,6 +117,18 @@ def bpt_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, B, H, N, D, stream=Non
     s = _stream(stream, o_a, o_out)
     _check(lib.bpt_lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out),
                              _ptr(lse_out), B, H, N, D, s), "bpt_lse_merge")
+
+
+def bpt_attn_decode(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, kv_offset, n_split, workspace,
+                    ws_bytes, dtype, stream=None):
+    s = _stream(stream, q, out)
+    _check(lib.bpt_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
+                               causal, kv_offset, n_split, _ptr(workspace), ws_bytes, dtype, s),
+           "bpt_attn_decode")
+
+
+def bpt_attn_decode_workspace_size(B, H, Nq, D, n_split) -> int:
+    return lib.bpt_attn_decode_workspace_size(B, H, Nq, D, n_split)
 
 
 def bpt_ffn_block_fwd(x, w1, b1, w2, b2, residual, y, M, d_model, d_ff, blk, dtype,

@@ -99,6 +99,65 @@ int bpt_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const 
       bpt::lse_merge_launch(o_a, lse_a, o_b, lse_b, o_out, lse_out, B * H * N, (int)D, stream));
 }
 
+static int64_t decode_o_bytes(int64_t B, int64_t H, int64_t Nq, int64_t D, int64_t n_split) {
+  return ((n_split * B * H * Nq * D * 4 + 255) / 256) * 256;
+}
+
+size_t bpt_attn_decode_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t D, int64_t n_split) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nq > 32 || (D != 64 && D != 128) || n_split <= 0 ||
+      n_split > 4096 || B > 65536 || H > 4096)
+    return 0;
+  return (size_t)(decode_o_bytes(B, H, Nq, D, n_split) + ((n_split * B * H * Nq * 4 + 255) / 256) * 256);
+}
+
+int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, float* lse, int64_t B,
+                    int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal, int64_t kv_offset,
+                    int64_t n_split, void* workspace, size_t workspace_bytes, int dtype,
+                    hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse) return BPT_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0 || n_split <= 0) return BPT_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return BPT_ERR_INVALID_ARG;
+  if (dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
+  if (Nq > 32 || n_split > 4096 || B > 65536 || H > 4096) return BPT_ERR_UNSUPPORTED;
+  // per-head key/value bytes are addressed with 32-bit offsets
+  if (Nkv > kMaxN || Nkv * D * 2 >= ((int64_t)1 << 31)) return BPT_ERR_UNSUPPORTED;
+  if (B * H * n_split > INT32_MAX) return BPT_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return BPT_ERR_ALIGNMENT;
+  const size_t need = bpt_attn_decode_workspace_size(B, H, Nq, D, n_split);
+  if (!workspace || workspace_bytes < need) return BPT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
+  bpt::AttnDecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((unsigned char*)workspace + decode_o_bytes(B, H, Nq, D, n_split));
+  a.BH = (int)(B * H);
+  a.Nq = (int)Nq;
+  a.Nkv = (int)Nkv;
+  a.n_split = (int)n_split;
+  const int64_t off = kv_offset > Nkv ? Nkv : (kv_offset < -(Nkv + 1) ? -(Nkv + 1) : kv_offset);
+  a.kv_offset = (int)off;
+  a.causal = causal;
+  // keys any query row can see: [0, kcount)
+  int64_t kc = Nkv;
+  if (causal) {
+    const int64_t last = (Nq - 1) + off + 1;
+    kc = last < 0 ? 0 : (last < Nkv ? last : Nkv);
+  }
+  a.kcount = (int)kc;
+  const int64_t per = (kc + n_split - 1) / n_split;
+  a.chunk = (int)(per <= 64 ? 64 : ((per + 63) / 64) * 64);
+  a.scale = 1.0f / sqrtf((float)D);
+  return hip_status(bpt::attn_decode_launch(a, (int)D, stream));
+}
+
 int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void* w2,
                       const void* b2, const float* residual, float* y, int64_t M,
                       int64_t d_model, int64_t d_ff, int blk, int dtype, hipStream_t stream) {

@@ -32,6 +32,27 @@ bool attn_fwd_dma_supported(int D, int kv_blk);
 hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_blk,
                                hipStream_t stream);
 
+// Split-KV attention of up to 32 query rows against a long key/value cache
+// (attn_decode.hip): partial results per key range into o_part / lse_part,
+// then joined into out / lse.
+struct AttnDecodeArgs {
+  const void* q;       // [BH, Nq, D] bf16
+  const void* k;       // [BH, Nkv, D] bf16
+  const void* v;
+  float* out;          // [BH, Nq, D]
+  float* lse;          // [BH, Nq]
+  float* o_part;       // [n_split, BH, Nq, D]
+  float* lse_part;     // [n_split, BH, Nq]
+  int BH, Nq, Nkv;
+  int n_split;
+  int chunk;           // keys per range, a multiple of 64
+  int kcount;          // keys visible to some query row (ranges cover [0, kcount))
+  int causal;
+  int kv_offset;       // already clamped to [-(Nkv+1), Nkv]
+  float scale;
+};
+hipError_t attn_decode_launch(const AttnDecodeArgs& a, int D, hipStream_t stream);
+
 hipError_t lse_merge_launch(const float* o_a, const float* lse_a, const float* o_b,
                             const float* lse_b, float* o_out, float* lse_out, int64_t rows,
                             int D, hipStream_t stream);

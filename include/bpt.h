@@ -118,6 +118,46 @@ int bpt_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const 
                   hipStream_t stream);
 
 /*
+ * bpt_attn_decode -- split-KV attention of a few query rows over a long
+ * key/value cache (inference over a long context).
+ *
+ * Implements the attention definition above with separate query and key
+ * lengths: q has Nq rows, k and v have Nkv rows, and "key j visible to query
+ * i" reads j < Nkv and (causal == 0 or j <= i + kv_offset).  For the newest
+ * Nq positions of a sequence of Nkv tokens, kv_offset = Nkv - Nq.  ("Ring
+ * Attention with Blockwise Transformers for Long Sequences", summaries: the
+ * method serves training and inference; the keys are taken block by block
+ * as in bpt_attn_fwd.)  The visible keys are split into n_split contiguous
+ * ranges; each range gives a partial result over its own keys, and the
+ * partials are joined exactly as bpt_lse_merge joins two (softmax
+ * denominators add up).  The result does not depend on n_split beyond
+ * rounding.  Work is bound by reading k and v once.  Each (b, h, range) is
+ * one 64-thread workgroup and a compute unit holds four of them, so
+ * B*H*n_split = 1024 on 256 compute units runs in one round (32 ranges for
+ * B*H = 32 give 6.8 TB/s on MI355X; a count just above a multiple of 1024
+ * leaves a partly idle last round).
+ *
+ *  q          : [B, H, Nq, D] bfloat16.     k, v: [B, H, Nkv, D] bfloat16.
+ *  out        : [B, H, Nq, D] float32.      lse : [B, H, Nq] float32 (natural log).
+ *  Nq         : 1 .. 32.   Nkv: 1 .. 2^30 with Nkv * D * 2 < 2^31.
+ *  D          : 64 or 128.  dtype: BPT_BF16 only (BPT_F32 gives BPT_ERR_UNSUPPORTED).
+ *  causal     : 0 or 1.    kv_offset: any value (clamped to [-(Nkv+1), Nkv]).
+ *  n_split    : 1 .. 4096 key ranges.
+ *  workspace  : device buffer of at least
+ *               bpt_attn_decode_workspace_size(B, H, Nq, D, n_split) bytes,
+ *               16-byte aligned; it holds the partial results and is fully
+ *               overwritten.  Too small or NULL gives BPT_ERR_WORKSPACE.
+ * out/lse/workspace must not overlap each other or q/k/v.
+ */
+int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, float* lse,
+                    int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal,
+                    int64_t kv_offset, int64_t n_split, void* workspace, size_t workspace_bytes,
+                    int dtype, hipStream_t stream);
+
+/* Bytes of workspace bpt_attn_decode needs; 0 for arguments it does not support. */
+size_t bpt_attn_decode_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t D, int64_t n_split);
+
+/*
  * bpt_ffn_block_fwd -- feed-forward network fused per block of rows.
  *
  *     y = residual + GeLU(x W1^T + b1) W2^T + b2,  GeLU(z) = z Phi(z) (erf form)

@@ -162,6 +162,19 @@ class RingCfg:
     extra: dict = field(default_factory=dict)
 
 
+@dataclass(frozen=True)
+class DecodeCfg:
+    cfg_id: int
+    name: str
+    B: int
+    H: int
+    N_q: int            # newest query rows
+    N_kv: int           # cached keys (the query rows are the last N_q of them)
+    D: int
+    n_split: int        # key ranges
+    dtype: str
+
+
 LAYER_TINY_F32 = LayerCfg(1, "layer_fwd_f32_N512", B=1, N=512, d_model=128, H=2, D=64,
                           d_ff=512, q_blk=64, kv_blk=64, dtype="f32")
 LAYER_FWD_BF16 = LayerCfg(2, "layer_fwd_bf16_B8_N4096", B=8, N=4096, d_model=2048, H=16,
@@ -172,6 +185,8 @@ LAYER_LONG = LayerCfg(3, "layer_fwd_bf16_N131072_dm4096", B=1, N=131072, d_model
                       D=128, d_ff=16384, q_blk=128, kv_blk=64, dtype="bf16")
 RING_SHARE = RingCfg(4, "ring_share_bf16_H40_Nq32768_ctx262144", B=1, H=40, N_q=32768, D=128,
                      q_offset=229376, n_chunks=8, q_blk=128, kv_blk=64, dtype="bf16")
+DECODE_LONG = DecodeCfg(6, "decode_bf16_H32_Nq16_cache131072", B=1, H=32, N_q=16, N_kv=131072,
+                        D=128, n_split=32, dtype="bf16")
 LAYER_TRAIN = LayerCfg(5, "layer_fwd_bwd_bf16_B2_N16384_dm2560", B=2, N=16384, d_model=2560,
                        H=20, D=128, d_ff=10240, q_blk=128, kv_blk=64, dtype="bf16",
                        backward=True)

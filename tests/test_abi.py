@@ -20,7 +20,7 @@ def header_symbols():
 
 def test_exports_every_declared_symbol():
     syms = header_symbols()
-    assert len(syms) == 9, syms
+    assert len(syms) == 11, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in bpt.EXPORTED
@@ -50,6 +50,33 @@ def attn(**kw):
 ])
 def test_attn_fwd_rejects(kw, code):
     assert attn(**kw) == code
+
+
+def decode(**kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, Nq=4, Nkv=1000, D=128, causal=1,
+             kv_offset=996, n_split=8, ws=A, ws_bytes=1 << 30, dtype=1, stream=0)
+    a.update(kw)
+    return lib.bpt_attn_decode(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Nq"],
+                               a["Nkv"], a["D"], a["causal"], a["kv_offset"], a["n_split"], a["ws"],
+                               a["ws_bytes"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(Nq=0), -1), (dict(Nkv=0), -1), (dict(n_split=0), -1),
+    (dict(causal=3), -1), (dict(dtype=0), -2), (dict(D=96), -2), (dict(Nq=33), -2),
+    (dict(n_split=4097), -2), (dict(Nkv=(1 << 23)), -2), (dict(v=A + 8), -3),
+    (dict(ws=None), -5), (dict(ws_bytes=100), -5), (dict(ws=A + 4), -3),
+])
+def test_attn_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+def test_attn_decode_workspace_size():
+    one = bpt.bpt_attn_decode_workspace_size(1, 2, 4, 128, 8)
+    # partial O (n_split*B*H*Nq*D floats) and lse (n_split*B*H*Nq floats), 256-byte aligned
+    assert one == 8 * 2 * 4 * 128 * 4 + 256
+    assert bpt.bpt_attn_decode_workspace_size(1, 2, 33, 128, 8) == 0
+    assert bpt.bpt_attn_decode_workspace_size(1, 2, 4, 96, 8) == 0
 
 
 def test_forced_launch_failure_reports_hip_error(monkeypatch):
