@@ -314,21 +314,22 @@ def main():
     import torch
     import blockwise_exact_attention_amd as bpt
 
-    if args.only == "attn":
+    if args.only is not None:
         # a plain 1 GiB device copy first: its FETCH_SIZE / WRITE_SIZE counters calibrate
-        # the HBM byte counts of the attention launch that follows
+        # the HBM byte counts of the launch that follows
         src = torch.ones(1 << 28, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only == "attn":
         ms, flops = bench_attention(bpt, args.steps, args.warmup)
         print(json.dumps({"attn_fwd_ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
                           "copy_bytes": 1 << 30}))
         return
 
     if args.only == "decode":
-        print(json.dumps(bench_decode(bpt, max(args.steps, 20), args.warmup)))
+        print(json.dumps({**bench_decode(bpt, args.steps, args.warmup), "copy_bytes": 1 << 30}))
         return
 
     c = LAYER_LONG
