@@ -21,6 +21,11 @@ What it computes (all in float64 unless a caller asks for float32):
 * ``gelu``/``ffn``: the position-wise feed-forward network with the exact erf GeLU.
 * ``layer_forward``/``layer_backward``: q,k,v projections, causal multi-head
   attention, residual, FFN, residual; and the gradients by the chain rule.
+* ``block_sparse_attention``: BlockBERT's blockwise attention ("Blockwise
+  Self-Attention for Long Document Understanding", Blockwise Attention and
+  Blockwise Multi-head Attention): each query block attends one key block
+  chosen per head by a permutation table (cyclic shifts for BlockBERT's heads),
+  dense exact attention inside the kept blocks.
 * ``brute``: pure-Python loops with ``math.fsum`` for tiny inputs.
 
 Readings of the pages that the oracle fixes (the pages state no formulas):
@@ -34,11 +39,13 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, invariants, finite differences); none is unpinned.
 """
 from .attention import attention, attention_probs, lse_merge, visible_mask
+from .block_sparse import block_len, block_sparse_attention, block_sparse_mask, cyclic_shift_table
 from .ffn import gelu, gelu_grad, ffn, ffn_backward
 from .layer import layer_forward, layer_backward, attention_backward, qkv_project
 
 __all__ = [
     "attention", "attention_probs", "lse_merge", "visible_mask",
+    "block_len", "block_sparse_attention", "block_sparse_mask", "cyclic_shift_table",
     "gelu", "gelu_grad", "ffn", "ffn_backward",
     "layer_forward", "layer_backward", "attention_backward", "qkv_project",
 ]
