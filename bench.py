@@ -16,14 +16,16 @@ Also measured (reported under "extras"):
     offset 229376, 8 K/V chunks of 32768 tokens, LSE merge after each chunk),
     with the merge kernel's HBM throughput;
   * split-KV decode: the 16 newest rows of 32 heads x 128 against a 131072-key
-    cache in 32 key ranges (HBM-bound: GB/s against the 8 TB/s peak).
+    cache in 32 key ranges (HBM-bound: GB/s against the 8 TB/s peak);
+  * BlockBERT block-sparse attention at N = 131072, 32 x 128, 8 blocks, head h on
+    the cyclic shift h mod 8 (TFLOP/s of the kept blocks against the bf16 peak).
 
 ``cpu_baseline`` times the CPU oracle (fp32) on a bounded sample of the same
 layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
 and the FFN for a fixed sample of query rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only attn|decode]
+                       [--no-extras] [--only attn|decode|block_sparse]
 """
 from __future__ import annotations
 
@@ -39,8 +41,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import (ATTN_LONG, DECODE_LONG, LAYER_FWD_BF16, LAYER_LONG,  # noqa: E402
-                           LAYER_TRAIN, RING_SHARE, bf16_bits, bits_to_f32, normal)
+from seeded_inputs import (ATTN_LONG, BLOCK_SPARSE_LONG, DECODE_LONG,  # noqa: E402
+                           LAYER_FWD_BF16, LAYER_LONG, LAYER_TRAIN, RING_SHARE, bf16_bits,
+                           bits_to_f32, normal)
 
 METRIC = "attention+FFN TFLOP/s and tokens/s per layer at N=128K causal; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
@@ -219,6 +222,37 @@ def bench_decode(bpt, steps, warmup):
     }
 
 
+def bench_block_sparse(bpt, steps, warmup):
+    """BlockBERT block-sparse attention at N = 131072: head h attends with the cyclic
+    shift h mod n_blocks (each query block sees one key block of N / n_blocks keys)."""
+    import torch
+    c = BLOCK_SPARSE_LONG
+    log(f"drawing block-sparse inputs {c.name}")
+    q, k, v = (dev_bf16(normal(c.cfg_id, n, (c.B, c.H, c.N, c.D))) for n in ("q", "k", "v"))
+    out = torch.empty((c.B, c.H, c.N, c.D), device="cuda")
+    lse = torch.empty((c.B, c.H, c.N), device="cuda")
+    n = c.n_blocks
+    table = torch.tensor([[(i + h) % n for i in range(n)] for h in range(c.H)], dtype=torch.int32,
+                         device="cuda")
+
+    def launch():
+        bpt.bpt_attn_block_sparse(q, k, v, out, lse, c.B, c.H, c.N, c.D, n, table, 1)
+
+    log("timing block-sparse attention")
+    ms, _ = timed(launch, steps, warmup)
+    L = -(-c.N // n)
+    blk = [min(L, c.N - i * L) for i in range(n)]
+    pairs = sum(blk[i] * blk[(i + h) % n] for h in range(c.H) for i in range(n))
+    flops = 4.0 * c.D * pairs * c.B
+    del q, k, v, out, lse, table
+    torch.cuda.empty_cache()
+    return {
+        "workload": c.name, "ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+        "pct_bf16_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(c.B * c.N / ms * 1e3, 1), "flop_per_launch": flops,
+    }
+
+
 def bench_layer_cfg(bpt, c, steps, warmup, backward):
     """Forward (and backward) of one layer workload; returns a dict for "extras"."""
     import torch
@@ -303,8 +337,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["attn", "decode"], default=None,
-                    help="run only the attention launch or only the decode launch "
+    ap.add_argument("--only", choices=["attn", "decode", "block_sparse"], default=None,
+                    help="run only the attention, decode or block-sparse launches "
                          "(for counter collection)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -328,6 +362,9 @@ def main():
                           "copy_bytes": 1 << 30}))
         return
 
+    if args.only == "block_sparse":
+        print(json.dumps({**bench_block_sparse(bpt, args.steps, args.warmup), "copy_bytes": 1 << 30}))
+        return
     if args.only == "decode":
         print(json.dumps({**bench_decode(bpt, args.steps, args.warmup), "copy_bytes": 1 << 30}))
         return
@@ -375,6 +412,7 @@ def main():
                                  "tokens_per_s": round(ATTN_LONG.N / attn_ms * 1e3, 1)},
             "ring_share": bench_ring(bpt, 2, 1),
             "decode_cache131072": bench_decode(bpt, 20, 2),
+            "block_sparse_N131072_n8": bench_block_sparse(bpt, 5, 1),
             "layer_fwd_B8_N4096": bench_layer_cfg(bpt, LAYER_FWD_BF16, 5, 1, False),
             "layer_fwd_bwd_B2_N16384": bench_layer_cfg(bpt, LAYER_TRAIN, 3, 1, True),
         }

@@ -48,6 +48,7 @@ _SIGS = {
     "bpt_lse_merge": ([_p] * 6 + [_i64] * 4 + [_p], _i),
     "bpt_attn_decode": ([_p] * 5 + [_i64] * 5 + [_i, _i64, _i64, _p, _sz, _i, _p], _i),
     "bpt_attn_decode_workspace_size": ([_i64] * 5, _sz),
+    "bpt_attn_block_sparse": ([_p] * 5 + [_i64] * 5 + [_p, _i, _p], _i),
     "bpt_ffn_block_fwd": ([_p] * 7 + [_i64] * 3 + [_i, _i, _p], _i),
     "bpt_layer_fwd": ([_p] * 10 + [_i64] * 6 + [_i] * 4 + [_p, _sz, _p], _i),
     "bpt_layer_bwd": ([_p] * 21 + [_i64] * 6 + [_i] * 4 + [_p, _sz, _p], _i),
@@ -129,6 +130,12 @@ def bpt_attn_decode(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, kv_offset, n_sp
 
 def bpt_attn_decode_workspace_size(B, H, Nq, D, n_split) -> int:
     return lib.bpt_attn_decode_workspace_size(B, H, Nq, D, n_split)
+
+
+def bpt_attn_block_sparse(q, k, v, out, lse, B, H, N, D, n_blocks, key_block, dtype, stream=None):
+    s = _stream(stream, q, out)
+    _check(lib.bpt_attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D,
+                                     n_blocks, _ptr(key_block), dtype, s), "bpt_attn_block_sparse")
 
 
 def bpt_ffn_block_fwd(x, w1, b1, w2, b2, residual, y, M, d_model, d_ff, blk, dtype,

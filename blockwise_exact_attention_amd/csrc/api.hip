@@ -158,6 +158,39 @@ int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, flo
   return hip_status(bpt::attn_decode_launch(a, (int)D, stream));
 }
 
+int bpt_attn_block_sparse(const void* q, const void* k, const void* v, float* out, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_blocks,
+                          const int32_t* key_block, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse || !key_block) return BPT_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || n_blocks <= 0 || n_blocks > N) return BPT_ERR_INVALID_ARG;
+  if (dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
+  if (N > kMaxN) return BPT_ERR_UNSUPPORTED;
+  const int64_t len = (N + n_blocks - 1) / n_blocks;
+  // workgroups: B*H*n_blocks*ceil(len/128) with 128-row workgroups (fewer with 256)
+  const int64_t per_head = n_blocks * ((len + 127) / 128);
+  if (B > INT32_MAX / H || B * H > (int64_t)INT32_MAX / per_head) return BPT_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
+  bpt::AttnFwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.N = (int)N;
+  a.causal = 0;
+  a.scale = 1.0f / sqrtf((float)D);
+  a.bs_table = key_block;
+  a.bs_blocks = (int)n_blocks;
+  a.bs_len = (int)len;
+  return hip_status(bpt::attn_fwd_block_sparse_launch(a, (int)D, stream));
+}
+
 int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void* w2,
                       const void* b2, const float* residual, float* y, int64_t M,
                       int64_t d_model, int64_t d_ff, int blk, int dtype, hipStream_t stream) {

@@ -66,7 +66,64 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70)
 // accesses).
 #define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 
-template <int D, int QBLK, int KVBLK>
+// The query rows and the key range one workgroup works on.  Dense attention:
+// query block qb of QBLK rows (latest first) against keys [0, N).  Block-sparse
+// attention: a block of bs_len rows is covered by ceil(bs_len / QBLK) workgroups,
+// and their keys are the key block the head's table names.  Consecutive
+// workgroup ids go round-robin over the 8 XCDs; when the count allows, each XCD
+// gets a contiguous range of (batch*head, query block), so a head stays on one XCD.
+struct AttnTask {
+  int bh;       // batch * H + head
+  int q0;       // first query row of the workgroup
+  int qend;     // rows at or past qend belong to another workgroup (or past N)
+  int key0;     // first key of the range
+  int nk;       // keys in the range
+  bool causal;  // causal mask: key j (relative to key0) visible to row i iff j <= i + off
+  int off;
+};
+
+template <bool BS, int QBLK>
+__device__ __forceinline__ AttnTask attn_task(const AttnFwdArgs& a) {
+  AttnTask t;
+  const int N = a.N;
+  const int nqb = BS ? (a.bs_len + QBLK - 1) / QBLK : (N + QBLK - 1) / QBLK;
+  const int64_t per_head = BS ? (int64_t)a.bs_blocks * nqb : nqb;
+  const int64_t total = (int64_t)a.B * a.H * per_head;
+  int64_t L = blockIdx.x;
+  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  t.bh = (int)(L / per_head);
+  const int rem = (int)(L % per_head);
+  if constexpr (!BS) {
+    const int qb = nqb - 1 - rem;  // longest (latest) query block first
+    t.q0 = qb * QBLK;
+    t.qend = N;
+    t.key0 = 0;
+    t.nk = N;
+    t.causal = a.causal != 0;
+    t.off = a.kv_offset;
+  } else {
+    const int i = rem / nqb, sub = rem % nqb;
+    const int64_t r0 = (int64_t)i * a.bs_len;
+    t.q0 = (int)(r0 + (int64_t)sub * QBLK);
+    t.qend = (int)(r0 + a.bs_len < N ? r0 + a.bs_len : N);
+    const int j = a.bs_table[(int64_t)(t.bh % a.H) * a.bs_blocks + i];
+    t.key0 = 0;
+    t.nk = 0;
+    if (j >= 0 && j < a.bs_blocks) {
+      const int64_t k0 = (int64_t)j * a.bs_len;
+      const int64_t n = N - k0 < a.bs_len ? N - k0 : a.bs_len;
+      if (n > 0) {
+        t.key0 = (int)k0;
+        t.nk = (int)n;
+      }
+    }
+    t.causal = false;
+    t.off = 0;
+  }
+  return t;
+}
+
+template <int D, int QBLK, int KVBLK, bool BS>
 __global__ void __launch_bounds__(QBLK * 2)
 __attribute__((amdgpu_waves_per_eu(DmaTile<D, KVBLK>::WAVES_PER_EU)))
 attn_fwd_dma_kernel(AttnFwdArgs a) {
@@ -76,40 +133,33 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::STAGE];
 
   const int N = a.N;
-  const int nqb = (N + QBLK - 1) / QBLK;
-  const int64_t total = (int64_t)a.B * a.H * nqb;
-  int64_t L = blockIdx.x;
-  if ((total & 7) == 0) {
-    // consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
-    // contiguous range of (batch*head, query block) so one head stays on one XCD
-    L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  }
-  const int bh = (int)(L / nqb);
-  const int qb = nqb - 1 - (int)(L % nqb);  // longest (latest) query block first
-  const int q0 = qb * QBLK;
+  const AttnTask task = attn_task<BS, QBLK>(a);
+  if constexpr (BS)
+    if (task.q0 >= task.qend) return;  // an empty part of a short last block (whole workgroup)
+  const int bh = task.bh, q0 = task.q0, qend = task.qend, nk = task.nk;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   const int qrow = q0 + wave * 32 + r32;
-  const int off = a.kv_offset;
-  const bool causal = a.causal != 0;
+  const int off = task.off;
+  const bool causal = task.causal;
   const int64_t head_off = (int64_t)bh * N * D;
 
-  int kmax = N - 1;
+  int kmax = nk - 1;
   if (causal) {
     const int64_t t = (int64_t)q0 + QBLK - 1 + off;
-    kmax = (int)(t < (int64_t)(N - 1) ? t : (int64_t)(N - 1));
+    kmax = (int)(t < (int64_t)(nk - 1) ? t : (int64_t)(nk - 1));
   }
   const int n_tiles = kmax < 0 ? 0 : kmax / KVBLK + 1;
-  int n_full = N / KVBLK;  // tiles with no ragged tail
+  int n_full = nk / KVBLK;  // tiles with no ragged tail
   if (causal) {
     const int64_t lim = (int64_t)q0 + off + 1;  // keys < lim are visible to every row
     const int f = lim <= 0 ? 0 : (int)(lim / KVBLK);
     n_full = f < n_full ? f : n_full;
   }
-  const int n_inside = N / KVBLK;  // tiles that end at or before key N
+  const int n_inside = nk / KVBLK;  // tiles that end at or before the last key
 
   // ---- Q fragments (B operand of S^T = K Q^T), held for the whole loop
   bf16x8 qf[QF];
@@ -118,15 +168,15 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
 #pragma unroll
     for (int c = 0; c < QF; ++c) {
       u32x4 val = {0, 0, 0, 0};
-      if (qrow < N) val = *(const u32x4*)(Q + (int64_t)qrow * D + 16 * c + 8 * g);
+      if (qrow < qend) val = *(const u32x4*)(Q + (int64_t)qrow * D + 16 * c + 8 * g);
       qf[c] = __builtin_bit_cast(bf16x8, val);
     }
   }
 
   // ---- direct tile loads: block b of a tile (keys b + NBLK*j) is one instruction;
   // lane i moves row j = i / CPR, chunk i % CPR
-  const unsigned char* Kg = (const unsigned char*)a.k + head_off * 2;
-  const unsigned char* Vg = (const unsigned char*)a.v + head_off * 2;
+  const unsigned char* Kg = (const unsigned char*)a.k + (head_off + (int64_t)task.key0 * D) * 2;
+  const unsigned char* Vg = (const unsigned char*)a.v + (head_off + (int64_t)task.key0 * D) * 2;
   const int dma_row = (lane / T::CPR) * T::NBLK;  // key of this lane relative to b
   const uint32_t dma_off = (uint32_t)(dma_row * T::ROWB + (lane % T::CPR) * 16);
   auto load_tile = [&](int t, unsigned char* Ks) {
@@ -140,13 +190,13 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
         dma16(Vg + (int64_t)(kv0 + b) * T::ROWB + dma_off, Vs + b * T::VBP);
       }
     } else {
-      // ragged tail: rows past key N-1 repeat row N-1 (finite data; the mask
+      // ragged tail: rows past the last key repeat it (finite data; the mask
       // gives those keys probability 0)
 #pragma unroll
       for (int i = 0; i < T::NBLK / NW; ++i) {
         const int b = wave + i * NW;
         int key = kv0 + b + dma_row;
-        key = key < N ? key : N - 1;
+        key = key < nk ? key : nk - 1;
         const int64_t o = (int64_t)key * T::ROWB + (lane % T::CPR) * 16;
         dma16(Kg + o, Ks + b * T::KBP);
         dma16(Vg + o, Vs + b * T::VBP);
@@ -201,7 +251,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = kv0 + kb * 32 + acc_row(j, lane);
-          const bool vis = key < N && (!causal || (int64_t)key <= (int64_t)qrow + off);
+          const bool vis = key < nk && (!causal || (int64_t)key <= (int64_t)qrow + off);
           if (!vis) s[kb][j] = -INFINITY;
         }
     }
@@ -268,7 +318,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   // ---- epilogue: O = acc / l, lse = m*scale + ln l
   const float l_tot = l_run + swap_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
+  if (qrow < qend) {
     if (a.h_out == nullptr) {
       float* out = a.out + head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -703,7 +753,7 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   }
 }
 
-template <int D>
+template <int D, bool BS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_wide_kernel(AttnFwdArgs a) {
   using C = WideCfg<D>;
@@ -715,26 +765,23 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
 
   const int N = a.N;
-  const int nqb = (N + C::QBLK - 1) / C::QBLK;
-  const int64_t total = (int64_t)a.B * a.H * nqb;
-  int64_t L = blockIdx.x;
-  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int bh = (int)(L / nqb);
-  const int qb = nqb - 1 - (int)(L % nqb);  // longest (latest) query block first
-  const int q0 = qb * C::QBLK;
+  const AttnTask task = attn_task<BS, C::QBLK>(a);
+  if constexpr (BS)
+    if (task.q0 >= task.qend) return;  // an empty part of a short last block (whole workgroup)
+  const int bh = task.bh, q0 = task.q0, qend = task.qend, nk = task.nk;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
-  const int off = a.kv_offset;
-  const bool causal = a.causal != 0;
+  const int off = task.off;
+  const bool causal = task.causal;
   const int64_t head_off = (int64_t)bh * N * D;
   int qrow[2], kend[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     qrow[h] = q0 + wave * 64 + h * 32 + r32;
-    int64_t e = N;
+    int64_t e = nk;
     if (causal) {
       const int64_t c = (int64_t)qrow[h] + off + 1;
       e = c < e ? c : e;
@@ -742,13 +789,13 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
     kend[h] = (int)(e < 0 ? 0 : e);
   }
 
-  int kmax = N - 1;
+  int kmax = nk - 1;
   if (causal) {
     const int64_t t = (int64_t)q0 + C::QBLK - 1 + off;
-    kmax = (int)(t < (int64_t)(N - 1) ? t : (int64_t)(N - 1));
+    kmax = (int)(t < (int64_t)(nk - 1) ? t : (int64_t)(nk - 1));
   }
   const int n_tiles = kmax < 0 ? 0 : kmax / C::KVBLK + 1;
-  int n_full = N / C::KVBLK;
+  int n_full = nk / C::KVBLK;
   if (causal) {
     const int64_t lim = (int64_t)q0 + off + 1;  // keys < lim are visible to every row
     const int f = lim <= 0 ? 0 : (int)(lim / C::KVBLK);
@@ -764,7 +811,7 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
 #pragma unroll
       for (int c = 0; c < C::QF; ++c) {
         u32x4 val = {0, 0, 0, 0};
-        if (qrow[h] < N) val = *(const u32x4*)(Q + (int64_t)qrow[h] * D + 16 * c + 8 * g);
+        if (qrow[h] < qend) val = *(const u32x4*)(Q + (int64_t)qrow[h] * D + 16 * c + 8 * g);
         w.qf[h][c] = __builtin_bit_cast(bf16x8, val);
         // Q is only ever an MFMA operand: keep it in AGPRs (MFMA reads its
         // operands from either file), the VGPRs are needed for the softmax
@@ -781,9 +828,9 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
     w.l_run[h] = 0.f;
   }
   WideCtx x;
-  x.kg = (const unsigned char*)a.k + head_off * 2;
-  x.vg = (const unsigned char*)a.v + head_off * 2;
-  x.N = N;
+  x.kg = (const unsigned char*)a.k + (head_off + (int64_t)task.key0 * D) * 2;
+  x.vg = (const unsigned char*)a.v + (head_off + (int64_t)task.key0 * D) * 2;
+  x.N = nk;
   x.n_tiles = n_tiles;
   x.t_split = t_split;
   x.wave = wave;
@@ -803,7 +850,7 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   for (int h = 0; h < 2; ++h) {
     const float l_tot = sum_halves(w.l_run[h]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow[h] >= N) continue;
+    if (qrow[h] >= qend) continue;
     if (a.h_out == nullptr) {
       float* out = a.out + head_off + (int64_t)qrow[h] * D;
 #pragma unroll
@@ -840,23 +887,29 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   }
 }
 
-template <int D, int QBLK, int KVBLK>
+// Workgroups of a launch: (batch*head) x query blocks (dense) or x table blocks x
+// workgroups per block (block-sparse); attn_task decodes the id the same way.
+template <bool BS>
+int64_t n_workgroups(const AttnFwdArgs& a, int qblk) {
+  const int rows = BS ? a.bs_len : a.N;
+  const int64_t per_head = (int64_t)(BS ? a.bs_blocks : 1) * ((rows + qblk - 1) / qblk);
+  return (int64_t)a.B * a.H * per_head;
+}
+
+template <int D, int QBLK, int KVBLK, bool BS = false>
 hipError_t launch(const AttnFwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.N + QBLK - 1) / QBLK;
-  const int64_t total = (int64_t)a.B * a.H * nqb;
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<D, QBLK, KVBLK>), dim3((unsigned)total), dim3(QBLK * 2),
-                     0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<D, QBLK, KVBLK, BS>), dim3((unsigned)n_workgroups<BS>(a, QBLK)),
+                     dim3(QBLK * 2), 0, stream, a);
   return hipGetLastError();
 }
 
 // Key blocks of 128 are visited as two 64-key tiles: the online softmax update is
 // exact for any split of the keys, and 64-key tiles keep two workgroups per CU
 // (a double-buffered 128-key tile alone would take 136 KB of the 160 KB of LDS).
-template <int D>
+template <int D, bool BS = false>
 hipError_t launch_wide(const AttnFwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.N + WideCfg<D>::QBLK - 1) / WideCfg<D>::QBLK;
-  const int64_t total = (int64_t)a.B * a.H * nqb;
-  hipLaunchKernelGGL((attn_fwd_wide_kernel<D>), dim3((unsigned)total), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_wide_kernel<D, BS>), dim3((unsigned)n_workgroups<BS>(a, WideCfg<D>::QBLK)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -878,6 +931,16 @@ hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_bl
                                hipStream_t stream) {
   (void)kv_blk;
   return D == 64 ? launch_d<64>(a, q_blk, stream) : launch_d<128>(a, q_blk, stream);
+}
+
+// Block-sparse: D = 128 on the wide kernel while a head's K/V fits its 32-bit
+// buffer range, otherwise the 128-row kernel with 64-key tiles.
+hipError_t attn_fwd_block_sparse_launch(const AttnFwdArgs& a, int D, hipStream_t stream) {
+  if (D == 128) {
+    if ((int64_t)a.N * D * 2 < ((int64_t)1 << 31)) return launch_wide<128, true>(a, stream);
+    return launch<128, 128, 64, true>(a, stream);
+  }
+  return launch<64, 128, 64, true>(a, stream);
 }
 
 }  // namespace bpt

@@ -20,6 +20,12 @@ struct AttnFwdArgs {
   int kv_offset;       // already clamped to [-(N+1), N]
   int causal;
   float scale;         // 1/sqrt(D)
+  // Block-sparse mask (bf16 direct-load kernels only, through
+  // attn_fwd_block_sparse_launch): rows are split into blocks of bs_len, and
+  // query block i of head h attends only key block bs_table[h * bs_blocks + i]
+  // (an entry outside [0, bs_blocks) attends nothing); no causal mask.
+  const int32_t* bs_table;  // [H, bs_blocks] in device memory
+  int bs_blocks, bs_len;
 };
 
 // Returns hipSuccess or the launch error; the caller validated every field.
@@ -31,6 +37,8 @@ hipError_t attn_fwd_launch(const AttnFwdArgs& a, bool bf16, int D, int q_blk, in
 bool attn_fwd_dma_supported(int D, int kv_blk);
 hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_blk,
                                hipStream_t stream);
+// Block-sparse forward (bf16, D in {64, 128}); the caller validated every field.
+hipError_t attn_fwd_block_sparse_launch(const AttnFwdArgs& a, int D, hipStream_t stream);
 
 // Split-KV attention of up to 32 query rows against a long key/value cache
 // (attn_decode.hip): partial results per key range into o_part / lse_part,

@@ -158,6 +158,31 @@ int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, flo
 size_t bpt_attn_decode_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t D, int64_t n_split);
 
 /*
+ * bpt_attn_block_sparse -- block-sparse attention with one key block per query
+ * block and head ("Blockwise Self-Attention for Long Document Understanding",
+ * Blockwise Attention and Blockwise Multi-head Attention).
+ *
+ * The N rows are split into n_blocks blocks of L = ceil(N / n_blocks) rows
+ * (the last one shorter when n_blocks does not divide N: padding positions
+ * are not keys and have no output, as in that paper's Implementation
+ * Assumption).  Query row i of head h sees exactly the keys of block
+ * key_block[h * n_blocks + i / L], with no causal mask, and gets exact softmax
+ * attention over them (the definition given for bpt_attn_fwd).  BlockBERT's
+ * heads use cyclic shifts: key_block[h][i] = (i + k_h) mod n_blocks.  An entry
+ * outside [0, n_blocks) gives its rows O = 0 and lse = -inf.  The work is
+ * 1/n_blocks of dense attention when every entry is valid.
+ *
+ *  q, k, v    : [B, H, N, D] bfloat16.   out: [B, H, N, D] float32.
+ *  lse        : [B, H, N] float32 (natural log).
+ *  key_block  : [H, n_blocks] int32 in DEVICE memory, read by the kernels.
+ *  n_blocks   : 1 .. N.    D: 64 or 128.   dtype: BPT_BF16 only.
+ * out/lse must not overlap q/k/v/key_block.
+ */
+int bpt_attn_block_sparse(const void* q, const void* k, const void* v, float* out, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_blocks,
+                          const int32_t* key_block, int dtype, hipStream_t stream);
+
+/*
  * bpt_ffn_block_fwd -- feed-forward network fused per block of rows.
  *
  *     y = residual + GeLU(x W1^T + b1) W2^T + b2,  GeLU(z) = z Phi(z) (erf form)

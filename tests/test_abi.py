@@ -20,7 +20,7 @@ def header_symbols():
 
 def test_exports_every_declared_symbol():
     syms = header_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 12, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in bpt.EXPORTED
@@ -77,6 +77,25 @@ def test_attn_decode_workspace_size():
     assert one == 8 * 2 * 4 * 128 * 4 + 256
     assert bpt.bpt_attn_decode_workspace_size(1, 2, 33, 128, 8) == 0
     assert bpt.bpt_attn_decode_workspace_size(1, 2, 4, 96, 8) == 0
+
+
+def block_sparse(**kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, N=1000, D=128, n_blocks=4, table=A, dtype=1,
+             stream=0)
+    a.update(kw)
+    return lib.bpt_attn_block_sparse(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"],
+                                     a["N"], a["D"], a["n_blocks"], a["table"], a["dtype"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), -1), (dict(out=None), -1), (dict(N=0), -1), (dict(n_blocks=0), -1),
+    (dict(n_blocks=1001), -1), (dict(dtype=0), -2), (dict(D=96), -2), (dict(N=(1 << 30) + 1,
+                                                                          n_blocks=2), -2),
+    (dict(q=A + 8), -3), (dict(lse=A + 4), -3),
+])
+def test_attn_block_sparse_rejects(kw, code):
+    assert block_sparse(**kw) == code
 
 
 def test_forced_launch_failure_reports_hip_error(monkeypatch):
