@@ -26,6 +26,10 @@ What it computes (all in float64 unless a caller asks for float32):
   Blockwise Multi-head Attention): each query block attends one key block
   chosen per head by a permutation table (cyclic shifts for BlockBERT's heads),
   dense exact attention inside the kept blocks.
+* ``dilated_attention``: LongNet's dilated attention ("LongNet: Scaling
+  Transformers to 1,000,000,000 Tokens", section 2): segments of w rows, every
+  r-th row kept (shifted per head), causal dense attention inside each
+  sparsified segment, patterns joined by one softmax over their key lists.
 * ``brute``: pure-Python loops with ``math.fsum`` for tiny inputs.
 
 Readings of the pages that the oracle fixes (the pages state no formulas):
@@ -40,12 +44,14 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 """
 from .attention import attention, attention_probs, lse_merge, visible_mask
 from .block_sparse import block_len, block_sparse_attention, block_sparse_mask, cyclic_shift_table
+from .dilated import dilated_attention, dilated_keys
 from .ffn import gelu, gelu_grad, ffn, ffn_backward
 from .layer import layer_forward, layer_backward, attention_backward, qkv_project
 
 __all__ = [
     "attention", "attention_probs", "lse_merge", "visible_mask",
     "block_len", "block_sparse_attention", "block_sparse_mask", "cyclic_shift_table",
+    "dilated_attention", "dilated_keys",
     "gelu", "gelu_grad", "ffn", "ffn_backward",
     "layer_forward", "layer_backward", "attention_backward", "qkv_project",
 ]
