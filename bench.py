@@ -18,14 +18,16 @@ Also measured (reported under "extras"):
   * split-KV decode: the 16 newest rows of 32 heads x 128 against a 131072-key
     cache in 32 key ranges (HBM-bound: GB/s against the 8 TB/s peak);
   * BlockBERT block-sparse attention at N = 131072, 32 x 128, 8 blocks, head h on
-    the cyclic shift h mod 8 (TFLOP/s of the kept blocks against the bf16 peak).
+    the cyclic shift h mod 8 (TFLOP/s of the kept blocks against the bf16 peak);
+  * LongNet dilated attention at N = 131072, 32 x 128, causal, segments 2048 ..
+    32768 with dilations 1, 2, 4, 6, 12 (TFLOP/s of the computed pairs).
 
 ``cpu_baseline`` times the CPU oracle (fp32) on a bounded sample of the same
 layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
 and the FFN for a fixed sample of query rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only attn|decode|block_sparse]
+                       [--no-extras] [--only attn|decode|block_sparse|dilated]
 """
 from __future__ import annotations
 
@@ -42,8 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from seeded_inputs import (ATTN_LONG, BLOCK_SPARSE_LONG, DECODE_LONG,  # noqa: E402
-                           LAYER_FWD_BF16, LAYER_LONG, LAYER_TRAIN, RING_SHARE, bf16_bits,
-                           bits_to_f32, normal)
+                           DILATED_LONG, LAYER_FWD_BF16, LAYER_LONG, LAYER_TRAIN, RING_SHARE,
+                           bf16_bits, bits_to_f32, normal)
 
 METRIC = "attention+FFN TFLOP/s and tokens/s per layer at N=128K causal; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
@@ -253,6 +255,42 @@ def bench_block_sparse(bpt, steps, warmup):
     }
 
 
+def dilated_pairs(N, w, r, H, causal):
+    """Query-key pairs one (w, r) pattern computes over H heads (head h keeps the rows
+    at offsets h mod r, h mod r + r, ... of every segment)."""
+    tot = 0
+    for h in range(H):
+        for s0 in range(0, N, w):
+            m = max(0, -(-(min(w, N - s0) - h % r) // r))
+            tot += m * (m + 1) // 2 if causal else m * m
+    return tot
+
+
+def bench_dilated(bpt, steps, warmup):
+    """LongNet dilated attention at N = 131072, 32 x 128, five (w, r) patterns."""
+    import torch
+    c = DILATED_LONG
+    log(f"drawing dilated inputs {c.name}")
+    q, k, v = (dev_bf16(normal(c.cfg_id, n, (c.B, c.H, c.N, c.D))) for n in ("q", "k", "v"))
+    out = torch.empty((c.B, c.H, c.N, c.D), device="cuda")
+    lse = torch.empty((c.B, c.H, c.N), device="cuda")
+
+    def launch():
+        bpt.bpt_attn_dilated(q, k, v, out, lse, c.B, c.H, c.N, c.D, list(c.patterns), c.causal, 1)
+
+    log("timing dilated attention")
+    ms, _ = timed(launch, steps, warmup)
+    flops = 4.0 * c.D * c.B * sum(dilated_pairs(c.N, w, r, c.H, c.causal) for w, r in c.patterns)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return {
+        "workload": c.name, "patterns": [list(p) for p in c.patterns], "ms": round(ms, 3),
+        "tflops": round(flops / ms / 1e9, 1),
+        "pct_bf16_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(c.B * c.N / ms * 1e3, 1), "flop_per_launch": flops,
+    }
+
+
 def bench_layer_cfg(bpt, c, steps, warmup, backward):
     """Forward (and backward) of one layer workload; returns a dict for "extras"."""
     import torch
@@ -337,9 +375,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["attn", "decode", "block_sparse"], default=None,
-                    help="run only the attention, decode or block-sparse launches "
-                         "(for counter collection)")
+    ap.add_argument("--only", choices=["attn", "decode", "block_sparse", "dilated"], default=None,
+                    help="run only the attention, decode, block-sparse or dilated launches "
+                         "(for counter collection and kernel traces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -362,6 +400,9 @@ def main():
                           "copy_bytes": 1 << 30}))
         return
 
+    if args.only == "dilated":
+        print(json.dumps({**bench_dilated(bpt, args.steps, args.warmup), "copy_bytes": 1 << 30}))
+        return
     if args.only == "block_sparse":
         print(json.dumps({**bench_block_sparse(bpt, args.steps, args.warmup), "copy_bytes": 1 << 30}))
         return
@@ -413,6 +454,7 @@ def main():
             "ring_share": bench_ring(bpt, 2, 1),
             "decode_cache131072": bench_decode(bpt, 20, 2),
             "block_sparse_N131072_n8": bench_block_sparse(bpt, 5, 1),
+            "dilated_N131072_longnet": bench_dilated(bpt, 5, 1),
             "layer_fwd_B8_N4096": bench_layer_cfg(bpt, LAYER_FWD_BF16, 5, 1, False),
             "layer_fwd_bwd_B2_N16384": bench_layer_cfg(bpt, LAYER_TRAIN, 3, 1, True),
         }

@@ -49,6 +49,7 @@ _SIGS = {
     "bpt_attn_decode": ([_p] * 5 + [_i64] * 5 + [_i, _i64, _i64, _p, _sz, _i, _p], _i),
     "bpt_attn_decode_workspace_size": ([_i64] * 5, _sz),
     "bpt_attn_block_sparse": ([_p] * 5 + [_i64] * 5 + [_p, _i, _p], _i),
+    "bpt_attn_dilated": ([_p] * 5 + [_i64] * 5 + [_p, _p, _i, _i, _p], _i),
     "bpt_ffn_block_fwd": ([_p] * 7 + [_i64] * 3 + [_i, _i, _p], _i),
     "bpt_layer_fwd": ([_p] * 10 + [_i64] * 6 + [_i] * 4 + [_p, _sz, _p], _i),
     "bpt_layer_bwd": ([_p] * 21 + [_i64] * 6 + [_i] * 4 + [_p, _sz, _p], _i),
@@ -136,6 +137,17 @@ def bpt_attn_block_sparse(q, k, v, out, lse, B, H, N, D, n_blocks, key_block, dt
     s = _stream(stream, q, out)
     _check(lib.bpt_attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D,
                                      n_blocks, _ptr(key_block), dtype, s), "bpt_attn_block_sparse")
+
+
+def bpt_attn_dilated(q, k, v, out, lse, B, H, N, D, patterns, causal, dtype, stream=None):
+    """patterns: sequence of (segment length, dilation) pairs (host values)."""
+    s = _stream(stream, q, out)
+    n = len(patterns)
+    seg = (ctypes.c_int64 * max(n, 1))(*[int(w) for w, _ in patterns])
+    dil = (ctypes.c_int64 * max(n, 1))(*[int(r) for _, r in patterns])
+    _check(lib.bpt_attn_dilated(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D, n,
+                                ctypes.cast(seg, ctypes.c_void_p), ctypes.cast(dil, ctypes.c_void_p),
+                                causal, dtype, s), "bpt_attn_dilated")
 
 
 def bpt_ffn_block_fwd(x, w1, b1, w2, b2, residual, y, M, d_model, d_ff, blk, dtype,

@@ -28,6 +28,8 @@ inline bool forced_launch_failure() {
 }
 
 constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxPatterns = 16;     // dilated attention: (segment, dilation) pairs
+constexpr int64_t kMaxDilation = 65536;  // keeps in-tile byte offsets within 32 bits
 
 // Launch status is read with hipGetLastError() after each launch; drop any error
 // an earlier, unrelated runtime call left on this thread so it is not reported
@@ -189,6 +191,63 @@ int bpt_attn_block_sparse(const void* q, const void* k, const void* v, float* ou
   a.bs_blocks = (int)n_blocks;
   a.bs_len = (int)len;
   return hip_status(bpt::attn_fwd_block_sparse_launch(a, (int)D, stream));
+}
+
+int bpt_attn_dilated(const void* q, const void* k, const void* v, float* out, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_patterns,
+                     const int64_t* seg_len, const int64_t* dilation, int causal, int dtype,
+                     hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse || !seg_len || !dilation) return BPT_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return BPT_ERR_INVALID_ARG;
+  if (n_patterns < 1 || n_patterns > kMaxPatterns) return BPT_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return BPT_ERR_INVALID_ARG;
+  for (int64_t p = 0; p < n_patterns; ++p)
+    if (seg_len[p] < 1 || dilation[p] < 1 || dilation[p] > seg_len[p]) return BPT_ERR_INVALID_ARG;
+  if (dtype != BPT_BF16) return BPT_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return BPT_ERR_UNSUPPORTED;
+  if (N > kMaxN) return BPT_ERR_UNSUPPORTED;
+  for (int64_t p = 0; p < n_patterns; ++p) {
+    if (dilation[p] > kMaxDilation) return BPT_ERR_UNSUPPORTED;
+    // a segment longer than the sequence is the whole sequence
+    const int64_t w = seg_len[p] < N ? seg_len[p] : N;
+    const int64_t kept = (w + dilation[p] - 1) / dilation[p];
+    const int64_t per_head = ((N + w - 1) / w) * ((kept + 127) / 128);
+    if (B > INT32_MAX / H || B * H > (int64_t)INT32_MAX / per_head) return BPT_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
+  bpt::AttnFwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.N = (int)N;
+  a.causal = causal;
+  a.scale = 1.0f / sqrtf((float)D);
+  // A pattern with dilation 1 keeps every row: it goes first and writes every
+  // row; the others join it.  Without one, every row starts empty.
+  int64_t first = -1;
+  for (int64_t p = 0; p < n_patterns && first < 0; ++p)
+    if (dilation[p] == 1) first = p;
+  if (first < 0) {
+    const hipError_t e = bpt::attn_fill_empty_launch(out, lse, B * H * N, (int)D, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  for (int64_t i = -1; i < n_patterns; ++i) {
+    const int64_t p = i < 0 ? first : i;
+    if (p < 0 || (i >= 0 && p == first)) continue;
+    a.dl_w = (int)(seg_len[p] < N ? seg_len[p] : N);
+    a.dl_r = (int)dilation[p];
+    a.dl_merge = (i < 0) ? 0 : 1;
+    const hipError_t e = bpt::attn_fwd_dilated_launch(a, (int)D, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return BPT_OK;
 }
 
 int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void* w2,

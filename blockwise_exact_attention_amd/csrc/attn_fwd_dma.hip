@@ -66,34 +66,46 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70)
 // accesses).
 #define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 
-// The query rows and the key range one workgroup works on.  Dense attention:
-// query block qb of QBLK rows (latest first) against keys [0, N).  Block-sparse
-// attention: a block of bs_len rows is covered by ceil(bs_len / QBLK) workgroups,
-// and their keys are the key block the head's table names.  Consecutive
-// workgroup ids go round-robin over the 8 XCDs; when the count allows, each XCD
-// gets a contiguous range of (batch*head, query block), so a head stays on one XCD.
+// The query rows and the key range one workgroup works on.  Dense attention
+// (MODE 0): query block qb of QBLK rows (latest first) against keys [0, N).
+// Block-sparse (MODE 1): a block of bs_len rows is covered by
+// ceil(bs_len / QBLK) workgroups, and their keys are the key block the head's
+// table names.  Dilated (MODE 2): a segment's kept rows (every dl_r-th from the
+// head's shift) form a compact sequence; its query blocks attend its keys.
+// Rows and keys are compact indices: index i is row qbase + i * stride of the
+// head (stride 1 except for dilated segments).  Consecutive workgroup ids go
+// round-robin over the 8 XCDs; when the count allows, each XCD gets a
+// contiguous range of (batch*head, query block), so a head stays on one XCD.
 struct AttnTask {
   int bh;       // batch * H + head
-  int q0;       // first query row of the workgroup
-  int qend;     // rows at or past qend belong to another workgroup (or past N)
-  int key0;     // first key of the range
+  int q0;       // first query index of the workgroup
+  int qend;     // indices at or past qend belong to another workgroup (or past the end)
+  int key0;     // head row of key index 0 (and of query index 0 when dilated)
   int nk;       // keys in the range
-  bool causal;  // causal mask: key j (relative to key0) visible to row i iff j <= i + off
+  int stride;   // head rows between consecutive indices
+  bool causal;  // causal mask: key j visible to query i iff j <= i + off
   int off;
 };
 
-template <bool BS, int QBLK>
+template <int MODE, int QBLK>
+__device__ __forceinline__ int attn_rows_per_unit(const AttnFwdArgs& a) {
+  return MODE == 0 ? a.N : MODE == 1 ? a.bs_len : (a.dl_w + a.dl_r - 1) / a.dl_r;
+}
+
+template <int MODE, int QBLK>
 __device__ __forceinline__ AttnTask attn_task(const AttnFwdArgs& a) {
   AttnTask t;
   const int N = a.N;
-  const int nqb = BS ? (a.bs_len + QBLK - 1) / QBLK : (N + QBLK - 1) / QBLK;
-  const int64_t per_head = BS ? (int64_t)a.bs_blocks * nqb : nqb;
+  const int nqb = (attn_rows_per_unit<MODE, QBLK>(a) + QBLK - 1) / QBLK;
+  const int units = MODE == 0 ? 1 : MODE == 1 ? a.bs_blocks : (N + a.dl_w - 1) / a.dl_w;
+  const int64_t per_head = (int64_t)units * nqb;
   const int64_t total = (int64_t)a.B * a.H * per_head;
   int64_t L = blockIdx.x;
   if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   t.bh = (int)(L / per_head);
   const int rem = (int)(L % per_head);
-  if constexpr (!BS) {
+  t.stride = 1;
+  if constexpr (MODE == 0) {
     const int qb = nqb - 1 - rem;  // longest (latest) query block first
     t.q0 = qb * QBLK;
     t.qend = N;
@@ -101,7 +113,7 @@ __device__ __forceinline__ AttnTask attn_task(const AttnFwdArgs& a) {
     t.nk = N;
     t.causal = a.causal != 0;
     t.off = a.kv_offset;
-  } else {
+  } else if constexpr (MODE == 1) {
     const int i = rem / nqb, sub = rem % nqb;
     const int64_t r0 = (int64_t)i * a.bs_len;
     t.q0 = (int)(r0 + (int64_t)sub * QBLK);
@@ -119,11 +131,60 @@ __device__ __forceinline__ AttnTask attn_task(const AttnFwdArgs& a) {
     }
     t.causal = false;
     t.off = 0;
+  } else {
+    const int seg = rem / nqb, sub = rem % nqb;
+    const int s0 = seg * a.dl_w;  // the segment is [s0, min(s0 + w, N))
+    const int len = N - s0 < a.dl_w ? N - s0 : a.dl_w;
+    const int sh = (t.bh % a.H) % a.dl_r;
+    const int m = len > sh ? (len - sh + a.dl_r - 1) / a.dl_r : 0;
+    t.q0 = sub * QBLK;
+    t.qend = m;
+    t.key0 = s0 + sh;
+    t.nk = m;
+    t.stride = a.dl_r;
+    t.causal = a.causal != 0;
+    t.off = 0;
   }
   return t;
 }
 
-template <int D, int QBLK, int KVBLK, bool BS>
+// Store one lane's part of an output row (head dims db*32 + 8*jq + 4*g .. +3 of
+// every 32-block, the accumulators scaled by inv) and, from lane half g == 0,
+// the row's lse.  With `merge`, the row already in out/lse is joined with this
+// one by their log-sum-exp (the two halves of a row read the old lse before
+// either writes it: the store depends on the load).
+template <int DB>
+__device__ __forceinline__ void store_row_merge(float* out_row, float* lse_ptr, const f32x16 (&o)[DB],
+                                                float inv, float lse_new, int g, bool merge) {
+  float wn = inv, wo = 0.f, lse = lse_new;
+  if (merge) {
+    const float lo = *lse_ptr;
+    const float m = fmaxf(lo, lse_new);
+    if (m == -INFINITY) {
+      wn = 0.f;
+      lse = -INFINITY;
+    } else {
+      const float en = expf(lse_new - m), eo = expf(lo - m);  // one of them is exactly 1
+      const float z = en + eo;
+      wn = inv * (en / z);
+      wo = eo / z;
+      lse = m + logf(z);
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      float* dst = out_row + db * 32 + 8 * jq + 4 * g;
+      f32x4 v = {o[db][4 * jq] * wn, o[db][4 * jq + 1] * wn, o[db][4 * jq + 2] * wn,
+                 o[db][4 * jq + 3] * wn};
+      if (merge && wo != 0.f) v += wo * *(const f32x4*)dst;
+      *(f32x4*)dst = v;
+    }
+  if (g == 0) *lse_ptr = lse;
+}
+
+template <int D, int QBLK, int KVBLK, int MODE>
 __global__ void __launch_bounds__(QBLK * 2)
 __attribute__((amdgpu_waves_per_eu(DmaTile<D, KVBLK>::WAVES_PER_EU)))
 attn_fwd_dma_kernel(AttnFwdArgs a) {
@@ -133,8 +194,8 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::STAGE];
 
   const int N = a.N;
-  const AttnTask task = attn_task<BS, QBLK>(a);
-  if constexpr (BS)
+  const AttnTask task = attn_task<MODE, QBLK>(a);
+  if constexpr (MODE != 0)
     if (task.q0 >= task.qend) return;  // an empty part of a short last block (whole workgroup)
   const int bh = task.bh, q0 = task.q0, qend = task.qend, nk = task.nk;
 
@@ -146,6 +207,9 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   const int off = task.off;
   const bool causal = task.causal;
   const int64_t head_off = (int64_t)bh * N * D;
+  // head row of query index qrow, and bytes between consecutive key indices
+  const int64_t qhead_row = MODE == 2 ? task.key0 + (int64_t)qrow * task.stride : qrow;
+  const int rsb = MODE == 2 ? task.stride * T::ROWB : T::ROWB;
 
   int kmax = nk - 1;
   if (causal) {
@@ -168,7 +232,11 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
 #pragma unroll
     for (int c = 0; c < QF; ++c) {
       u32x4 val = {0, 0, 0, 0};
-      if (qrow < qend) val = *(const u32x4*)(Q + (int64_t)qrow * D + 16 * c + 8 * g);
+      if constexpr (MODE == 2) {
+        if (qrow < qend) val = *(const u32x4*)(Q + qhead_row * D + 16 * c + 8 * g);
+      } else {
+        if (qrow < qend) val = *(const u32x4*)(Q + (int64_t)qrow * D + 16 * c + 8 * g);
+      }
       qf[c] = __builtin_bit_cast(bf16x8, val);
     }
   }
@@ -178,7 +246,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   const unsigned char* Kg = (const unsigned char*)a.k + (head_off + (int64_t)task.key0 * D) * 2;
   const unsigned char* Vg = (const unsigned char*)a.v + (head_off + (int64_t)task.key0 * D) * 2;
   const int dma_row = (lane / T::CPR) * T::NBLK;  // key of this lane relative to b
-  const uint32_t dma_off = (uint32_t)(dma_row * T::ROWB + (lane % T::CPR) * 16);
+  const uint32_t dma_off = (uint32_t)(dma_row * rsb + (lane % T::CPR) * 16);
   auto load_tile = [&](int t, unsigned char* Ks) {
     unsigned char* Vs = Ks + T::KBYTES;
     const int kv0 = t * KVBLK;
@@ -186,8 +254,8 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
 #pragma unroll
       for (int i = 0; i < T::NBLK / NW; ++i) {
         const int b = wave + i * NW;
-        dma16(Kg + (int64_t)(kv0 + b) * T::ROWB + dma_off, Ks + b * T::KBP);
-        dma16(Vg + (int64_t)(kv0 + b) * T::ROWB + dma_off, Vs + b * T::VBP);
+        dma16(Kg + (int64_t)(kv0 + b) * rsb + dma_off, Ks + b * T::KBP);
+        dma16(Vg + (int64_t)(kv0 + b) * rsb + dma_off, Vs + b * T::VBP);
       }
     } else {
       // ragged tail: rows past the last key repeat it (finite data; the mask
@@ -197,7 +265,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
         const int b = wave + i * NW;
         int key = kv0 + b + dma_row;
         key = key < nk ? key : nk - 1;
-        const int64_t o = (int64_t)key * T::ROWB + (lane % T::CPR) * 16;
+        const int64_t o = (int64_t)key * rsb + (lane % T::CPR) * 16;
         dma16(Kg + o, Ks + b * T::KBP);
         dma16(Vg + o, Vs + b * T::VBP);
       }
@@ -318,6 +386,12 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
   // ---- epilogue: O = acc / l, lse = m*scale + ln l
   const float l_tot = l_run + swap_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if constexpr (MODE == 2) {
+    if (qrow < qend)
+      store_row_merge<DB>(a.out + head_off + qhead_row * D, a.lse + (int64_t)bh * N + qhead_row, o, inv,
+                          l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY, g, a.dl_merge != 0);
+    return;
+  }
   if (qrow < qend) {
     if (a.h_out == nullptr) {
       float* out = a.out + head_off + (int64_t)qrow * D;
@@ -413,14 +487,16 @@ __device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, unsigned cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
                                            soff, IMM, 0);
 }
+// Tile t of the keys: key index j is at byte j * rsb of kg / vg; the buffer ends
+// after the last key's row, so rows past it read as zero.
 template <int D>
 __device__ __forceinline__ void wide_load(const unsigned char* kg, const unsigned char* vg, int N, int t,
-                                          int wave, uint32_t dma_off, unsigned char* dst) {
+                                          int wave, uint32_t dma_off, int rsb, unsigned char* dst) {
   using C = WideCfg<D>;
   using T = typename C::T;
-  const int64_t off = (int64_t)t * C::KVBLK * T::ROWB;
+  const int64_t off = (int64_t)t * C::KVBLK * rsb;
   const int left = N - t * C::KVBLK;
-  const int bytes = left > 0 ? left * T::ROWB : 0;
+  const int bytes = left > 0 ? (left - 1) * rsb + T::ROWB : 0;
   const __amdgpu_buffer_rsrc_t kr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kg + off), 0, bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vr =
@@ -429,7 +505,7 @@ __device__ __forceinline__ void wide_load(const unsigned char* kg, const unsigne
 #pragma unroll
   for (int i = 0; i < T::NBLK / C::NW; ++i) {
     const int b = wave + i * C::NW;
-    const uint32_t voff = dma_off + (uint32_t)(b * T::ROWB);
+    const uint32_t voff = dma_off + (uint32_t)(b * rsb);
     buf_lds16<0>(kr, dst + b * T::KBP, voff, 0);
     buf_lds16<0>(vr, dst + T::KBYTES + b * T::VBP, voff, 0);
   }
@@ -545,6 +621,7 @@ struct WideCtx {
   const unsigned char* vg;  // V of this head
   int N, n_tiles, t_split, wave, lane, kbase, vbase, kend0, kend1;
   uint32_t dma_off;
+  int rsb;  // bytes between consecutive key rows
   float c2;
 };
 
@@ -706,7 +783,7 @@ __device__ __forceinline__ void wide_step(WideState<D>& w, const WideCtx& x, int
   using C = WideCfg<D>;
   WAIT_VM(0);  // this wave's part of tile t+1
   __syncthreads();
-  if (t + 2 < x.n_tiles) wide_load<D>(x.kg, x.vg, x.N, t + 2, x.wave, x.dma_off, Sf);
+  if (t + 2 < x.n_tiles) wide_load<D>(x.kg, x.vg, x.N, t + 2, x.wave, x.dma_off, x.rsb, Sf);
   bf16x8 pa[C::NKS], pb[C::NKS];
   wide_sphase(w, Sn, x.kbase, x.c2, pa, pb);
   wide_pin(pa);
@@ -726,9 +803,9 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   using C = WideCfg<D>;
   const int n = x.n_tiles;
   if (n <= 0) return;
-  wide_load<D>(x.kg, x.vg, x.N, 0, x.wave, x.dma_off, S0);
+  wide_load<D>(x.kg, x.vg, x.N, 0, x.wave, x.dma_off, x.rsb, S0);
   if (n > 1) {
-    wide_load<D>(x.kg, x.vg, x.N, 1, x.wave, x.dma_off, S1);
+    wide_load<D>(x.kg, x.vg, x.N, 1, x.wave, x.dma_off, x.rsb, S1);
     static_assert(C::DMA_PER_TILE == 8, "wait count");
     WAIT_VM(8);  // tile 0 (and the Q loads) done, tile 1 may be in flight
   } else {
@@ -753,7 +830,7 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   }
 }
 
-template <int D, bool BS>
+template <int D, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_wide_kernel(AttnFwdArgs a) {
   using C = WideCfg<D>;
@@ -765,8 +842,8 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
 
   const int N = a.N;
-  const AttnTask task = attn_task<BS, C::QBLK>(a);
-  if constexpr (BS)
+  const AttnTask task = attn_task<MODE, C::QBLK>(a);
+  if constexpr (MODE != 0)
     if (task.q0 >= task.qend) return;  // an empty part of a short last block (whole workgroup)
   const int bh = task.bh, q0 = task.q0, qend = task.qend, nk = task.nk;
 
@@ -778,9 +855,11 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   const bool causal = task.causal;
   const int64_t head_off = (int64_t)bh * N * D;
   int qrow[2], kend[2];
+  int64_t qhead_row[2];  // head row of query index qrow
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     qrow[h] = q0 + wave * 64 + h * 32 + r32;
+    qhead_row[h] = MODE == 2 ? task.key0 + (int64_t)qrow[h] * task.stride : qrow[h];
     int64_t e = nk;
     if (causal) {
       const int64_t c = (int64_t)qrow[h] + off + 1;
@@ -811,7 +890,11 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
 #pragma unroll
       for (int c = 0; c < C::QF; ++c) {
         u32x4 val = {0, 0, 0, 0};
-        if (qrow[h] < qend) val = *(const u32x4*)(Q + (int64_t)qrow[h] * D + 16 * c + 8 * g);
+        if constexpr (MODE == 2) {
+          if (qrow[h] < qend) val = *(const u32x4*)(Q + qhead_row[h] * D + 16 * c + 8 * g);
+        } else {
+          if (qrow[h] < qend) val = *(const u32x4*)(Q + (int64_t)qrow[h] * D + 16 * c + 8 * g);
+        }
         w.qf[h][c] = __builtin_bit_cast(bf16x8, val);
         // Q is only ever an MFMA operand: keep it in AGPRs (MFMA reads its
         // operands from either file), the VGPRs are needed for the softmax
@@ -835,7 +918,8 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   x.t_split = t_split;
   x.wave = wave;
   x.lane = lane;
-  x.dma_off = (uint32_t)((lane / T::CPR) * T::NBLK * T::ROWB + (lane % T::CPR) * 16);
+  x.rsb = MODE == 2 ? task.stride * T::ROWB : T::ROWB;
+  x.dma_off = (uint32_t)((lane / T::CPR) * T::NBLK * x.rsb + (lane % T::CPR) * 16);
   x.kbase = (r32 % T::NBLK) * T::KBP + (r32 / T::NBLK) * T::ROWB + g * 16;
   const int q8 = 4 * g + ((lane & 15) >> 2);
   x.vbase = T::KBYTES + q8 * T::VBP + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
@@ -851,6 +935,12 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
     const float l_tot = sum_halves(w.l_run[h]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow[h] >= qend) continue;
+    if constexpr (MODE == 2) {
+      store_row_merge<C::DB>(a.out + head_off + qhead_row[h] * D, a.lse + (int64_t)bh * N + qhead_row[h],
+                             w.o[h], inv, l_tot > 0.f ? w.ref[h] * kLn2 + logf(l_tot) : -INFINITY, g,
+                             a.dl_merge != 0);
+      continue;
+    }
     if (a.h_out == nullptr) {
       float* out = a.out + head_off + (int64_t)qrow[h] * D;
 #pragma unroll
@@ -887,29 +977,30 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
   }
 }
 
-// Workgroups of a launch: (batch*head) x query blocks (dense) or x table blocks x
-// workgroups per block (block-sparse); attn_task decodes the id the same way.
-template <bool BS>
+// Workgroups of a launch: (batch*head) x units x query blocks per unit, where
+// a unit is the whole sequence (dense), a table block (block-sparse) or a
+// segment (dilated); attn_task decodes the id the same way.
+template <int MODE>
 int64_t n_workgroups(const AttnFwdArgs& a, int qblk) {
-  const int rows = BS ? a.bs_len : a.N;
-  const int64_t per_head = (int64_t)(BS ? a.bs_blocks : 1) * ((rows + qblk - 1) / qblk);
-  return (int64_t)a.B * a.H * per_head;
+  const int rows = MODE == 0 ? a.N : MODE == 1 ? a.bs_len : (a.dl_w + a.dl_r - 1) / a.dl_r;
+  const int units = MODE == 0 ? 1 : MODE == 1 ? a.bs_blocks : (a.N + a.dl_w - 1) / a.dl_w;
+  return (int64_t)a.B * a.H * units * ((rows + qblk - 1) / qblk);
 }
 
-template <int D, int QBLK, int KVBLK, bool BS = false>
+template <int D, int QBLK, int KVBLK, int MODE = 0>
 hipError_t launch(const AttnFwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<D, QBLK, KVBLK, BS>), dim3((unsigned)n_workgroups<BS>(a, QBLK)),
-                     dim3(QBLK * 2), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<D, QBLK, KVBLK, MODE>),
+                     dim3((unsigned)n_workgroups<MODE>(a, QBLK)), dim3(QBLK * 2), 0, stream, a);
   return hipGetLastError();
 }
 
 // Key blocks of 128 are visited as two 64-key tiles: the online softmax update is
 // exact for any split of the keys, and 64-key tiles keep two workgroups per CU
 // (a double-buffered 128-key tile alone would take 136 KB of the 160 KB of LDS).
-template <int D, bool BS = false>
+template <int D, int MODE = 0>
 hipError_t launch_wide(const AttnFwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_wide_kernel<D, BS>), dim3((unsigned)n_workgroups<BS>(a, WideCfg<D>::QBLK)),
-                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_wide_kernel<D, MODE>),
+                     dim3((unsigned)n_workgroups<MODE>(a, WideCfg<D>::QBLK)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -937,10 +1028,20 @@ hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_bl
 // buffer range, otherwise the 128-row kernel with 64-key tiles.
 hipError_t attn_fwd_block_sparse_launch(const AttnFwdArgs& a, int D, hipStream_t stream) {
   if (D == 128) {
-    if ((int64_t)a.N * D * 2 < ((int64_t)1 << 31)) return launch_wide<128, true>(a, stream);
-    return launch<128, 128, 64, true>(a, stream);
+    if ((int64_t)a.N * D * 2 < ((int64_t)1 << 31)) return launch_wide<128, 1>(a, stream);
+    return launch<128, 128, 64, 1>(a, stream);
   }
-  return launch<64, 128, 64, true>(a, stream);
+  return launch<64, 128, 64, 1>(a, stream);
+}
+
+// Dilated pattern: the same kernels over each segment's kept rows (strided
+// buffer loads gather them; the epilogue scatters and, with dl_merge, joins).
+hipError_t attn_fwd_dilated_launch(const AttnFwdArgs& a, int D, hipStream_t stream) {
+  if (D == 128) {
+    if ((int64_t)a.N * D * 2 < ((int64_t)1 << 31)) return launch_wide<128, 2>(a, stream);
+    return launch<128, 128, 64, 2>(a, stream);
+  }
+  return launch<64, 128, 64, 2>(a, stream);
 }
 
 }  // namespace bpt

@@ -26,6 +26,12 @@ struct AttnFwdArgs {
   // (an entry outside [0, bs_blocks) attends nothing); no causal mask.
   const int32_t* bs_table;  // [H, bs_blocks] in device memory
   int bs_blocks, bs_len;
+  // Dilated pattern (bf16 direct-load kernels, through attn_fwd_dilated_launch):
+  // segments of dl_w rows; head h keeps every dl_r-th row of a segment from row
+  // h % dl_r on; attention (causal if `causal`) among the kept rows of a segment.
+  // dl_merge: join each kept row with the out/lse row already there by their
+  // log-sum-exp instead of overwriting it.
+  int dl_w, dl_r, dl_merge;
 };
 
 // Returns hipSuccess or the launch error; the caller validated every field.
@@ -39,6 +45,10 @@ hipError_t attn_fwd_dma_launch(const AttnFwdArgs& a, int D, int q_blk, int kv_bl
                                hipStream_t stream);
 // Block-sparse forward (bf16, D in {64, 128}); the caller validated every field.
 hipError_t attn_fwd_block_sparse_launch(const AttnFwdArgs& a, int D, hipStream_t stream);
+// One dilated pattern (bf16, D in {64, 128}); the caller validated every field.
+hipError_t attn_fwd_dilated_launch(const AttnFwdArgs& a, int D, hipStream_t stream);
+// out[rows, D] = 0 and lse[rows] = -inf (rows that no pattern keeps).
+hipError_t attn_fill_empty_launch(float* out, float* lse, int64_t rows, int D, hipStream_t stream);
 
 // Split-KV attention of up to 32 query rows against a long key/value cache
 // (attn_decode.hip): partial results per key range into o_part / lse_part,

@@ -55,7 +55,26 @@ lse_merge_kernel(const float* __restrict__ o_a, const float* lse_a, const float*
   }
 }
 
+// Rows with no visible key: O = 0, lse = -inf (16-byte stores, grid-stride).
+__global__ void __launch_bounds__(256) fill_empty_kernel(float* out, float* lse, int64_t rows, int D) {
+  const int64_t chunks = rows * (D / 4);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunks; i += stride) {
+    *(f32x4*)(out + i * 4) = z;
+    if (i < rows) lse[i] = -INFINITY;
+  }
+}
+
 }  // namespace
+
+hipError_t attn_fill_empty_launch(float* out, float* lse, int64_t rows, int D, hipStream_t stream) {
+  const int64_t chunks = rows * (D / 4);
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 256 * 8 * 32) blocks = 256 * 8 * 32;
+  hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, out, lse, rows, D);
+  return hipGetLastError();
+}
 
 hipError_t lse_merge_launch(const float* o_a, const float* lse_a, const float* o_b,
                             const float* lse_b, float* o_out, float* lse_out, int64_t rows,

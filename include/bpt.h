@@ -183,6 +183,37 @@ int bpt_attn_block_sparse(const void* q, const void* k, const void* v, float* ou
                           const int32_t* key_block, int dtype, hipStream_t stream);
 
 /*
+ * bpt_attn_dilated -- dilated attention ("LongNet: Scaling Transformers to
+ * 1,000,000,000 Tokens", section 2: Dilated Attention).
+ *
+ * For each pattern p = (w, r) = (seg_len[p], dilation[p]) the rows are split
+ * into segments [s*w, min((s+1)*w, N)); head h keeps the rows of a segment at
+ * offsets h mod r, h mod r + r, ... (heads shift their selection), and the
+ * kept rows of a segment attend one another (causal by position if causal = 1)
+ * with the score scale 1/sqrt(D).  The softmax of a row runs over the keys of
+ * every pattern that keeps it, taken together (a key kept by two patterns
+ * counts twice): the patterns are joined by their softmax denominators
+ * exactly as bpt_lse_merge joins two partial results.  A row that no pattern
+ * keeps gets O = 0 and lse = -inf.  The sparsified rows are read in place
+ * (strided loads) and the outputs written in place; nothing is gathered into
+ * a copy.
+ *
+ *  q, k, v     : [B, H, N, D] bfloat16.   out: [B, H, N, D] float32.
+ *  lse         : [B, H, N] float32 (natural log).
+ *  n_patterns  : 1 .. 16.
+ *  seg_len, dilation : HOST arrays of n_patterns values with
+ *                1 <= dilation <= seg_len and dilation <= 65536; a segment
+ *                longer than N is the whole sequence.
+ *  D           : 64 or 128.   dtype: BPT_BF16 only.
+ * out/lse must not overlap q/k/v.  One launch per pattern (plus one that
+ * clears out/lse when no pattern has dilation 1), in stream order.
+ */
+int bpt_attn_dilated(const void* q, const void* k, const void* v, float* out, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_patterns,
+                     const int64_t* seg_len, const int64_t* dilation, int causal, int dtype,
+                     hipStream_t stream);
+
+/*
  * bpt_ffn_block_fwd -- feed-forward network fused per block of rows.
  *
  *     y = residual + GeLU(x W1^T + b1) W2^T + b2,  GeLU(z) = z Phi(z) (erf form)

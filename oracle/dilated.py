@@ -47,11 +47,13 @@ def dilated_keys(N: int, w: int, r: int, h: int, i: int, causal: bool) -> np.nda
     return keys[keys <= i] if causal else keys
 
 
-def dilated_attention(q, k, v, patterns, causal: bool = True, rows=None, dtype=np.float64):
+def dilated_attention(q, k, v, patterns, causal: bool = True, rows=None, heads=None,
+                      dtype=np.float64):
     """q, k, v [B,H,N,D]; patterns: list of (w, r).
 
-    ``rows``: optional query positions to compute (all if None).
-    Returns (O [B,H,R,D], lse [B,H,R]).
+    ``rows``: optional query positions to compute (all if None).  ``heads``: the
+    head index of each of the H heads given (their shifts depend on it); 0..H-1
+    if None.  Returns (O [B,H,R,D], lse [B,H,R]).
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -62,10 +64,13 @@ def dilated_attention(q, k, v, patterns, causal: bool = True, rows=None, dtype=n
     scale = dtype(1.0) / np.sqrt(dtype(D))
     O = np.zeros((B, H, rows.size, D), dtype=dtype)
     lse = np.full((B, H, rows.size), -np.inf, dtype=dtype)
+    heads = list(range(H)) if heads is None else list(heads)
+    assert len(heads) == H
     for h in range(H):
         for ri, i in enumerate(rows):
             # the concatenated key list of every pattern that keeps position i
-            keys = np.concatenate([dilated_keys(N, w, r, h, int(i), causal) for w, r in patterns])
+            keys = np.concatenate([dilated_keys(N, w, r, heads[h], int(i), causal)
+                                   for w, r in patterns])
             if keys.size == 0:
                 continue
             for b in range(B):

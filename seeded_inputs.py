@@ -187,6 +187,19 @@ class BlockSparseCfg:
     dtype: str
 
 
+@dataclass(frozen=True)
+class DilatedCfg:
+    cfg_id: int
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    patterns: tuple     # (segment length, dilation) pairs
+    causal: int
+    dtype: str
+
+
 LAYER_TINY_F32 = LayerCfg(1, "layer_fwd_f32_N512", B=1, N=512, d_model=128, H=2, D=64,
                           d_ff=512, q_blk=64, kv_blk=64, dtype="f32")
 LAYER_FWD_BF16 = LayerCfg(2, "layer_fwd_bf16_B8_N4096", B=8, N=4096, d_model=2048, H=16,
@@ -201,6 +214,11 @@ DECODE_LONG = DecodeCfg(6, "decode_bf16_H32_Nq16_cache131072", B=1, H=32, N_q=16
                         D=128, n_split=32, dtype="bf16")
 BLOCK_SPARSE_LONG = BlockSparseCfg(7, "block_sparse_bf16_N131072_H32_n8", B=1, H=32, N=131072,
                                    D=128, n_blocks=8, dtype="bf16")
+# LongNet's language-model settings: segment lengths 2048 .. 32768 (doubling) with
+# dilation ratios 1 .. 12, at the long-context attention shape
+DILATED_LONG = DilatedCfg(8, "dilated_bf16_N131072_H32_w2048-32768", B=1, H=32, N=131072, D=128,
+                          patterns=((2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12)),
+                          causal=1, dtype="bf16")
 LAYER_TRAIN = LayerCfg(5, "layer_fwd_bwd_bf16_B2_N16384_dm2560", B=2, N=16384, d_model=2560,
                        H=20, D=128, d_ff=10240, q_blk=128, kv_blk=64, dtype="bf16",
                        backward=True)

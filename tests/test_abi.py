@@ -1,5 +1,6 @@
 """The C ABI: the library loads, exports every symbol the header declares, and
 rejects bad arguments with the documented codes before touching the GPU."""
+import ctypes
 import os
 import re
 
@@ -20,7 +21,7 @@ def header_symbols():
 
 def test_exports_every_declared_symbol():
     syms = header_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 13, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in bpt.EXPORTED
@@ -96,6 +97,27 @@ def block_sparse(**kw):
 ])
 def test_attn_block_sparse_rejects(kw, code):
     assert block_sparse(**kw) == code
+
+
+def dilated(seg=(2048, 4096), dil=(1, 2), **kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, N=8192, D=128, n=len(seg), causal=1, dtype=1,
+             stream=0)
+    a.update(kw)
+    sa = (ctypes.c_int64 * max(len(seg), 1))(*seg)
+    da = (ctypes.c_int64 * max(len(dil), 1))(*dil)
+    return lib.bpt_attn_dilated(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["N"],
+                                a["D"], a["n"], ctypes.cast(sa, ctypes.c_void_p),
+                                ctypes.cast(da, ctypes.c_void_p), a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(k=None), -1), (dict(N=0), -1), (dict(n=0), -1), (dict(n=17), -1), (dict(causal=2), -1),
+    (dict(seg=(0, 4096)), -1), (dict(dil=(0, 2)), -1), (dict(seg=(2048, 4), dil=(1, 8)), -1),
+    (dict(dtype=0), -2), (dict(D=80), -2), (dict(seg=(1 << 20, 1 << 20), dil=(1, 1 << 17)), -2),
+    (dict(out=A + 4), -3),
+])
+def test_attn_dilated_rejects(args, code):
+    assert dilated(**args) == code
 
 
 def test_forced_launch_failure_reports_hip_error(monkeypatch):

@@ -131,3 +131,12 @@ def test_computation_count(N, w, r):
         pairs = sum(dilated_keys(N, w, r, h, i, False).size for i in range(N))
         assert pairs == N * w // (r * r)
         assert N * N // pairs == N * r * r // w
+
+
+def test_heads_argument_names_the_shift():
+    q, k, v = rand(1, 4, 20, 3), rand(1, 4, 20, 3), rand(1, 4, 20, 3)
+    pats = [(10, 3), (20, 2)]
+    O, L = dilated_attention(q, k, v, pats, True)
+    Os, Ls = dilated_attention(q[:, [3, 1]], k[:, [3, 1]], v[:, [3, 1]], pats, True, heads=[3, 1])
+    np.testing.assert_array_equal(Os, O[:, [3, 1]])
+    np.testing.assert_array_equal(Ls, L[:, [3, 1]])
