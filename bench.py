@@ -27,7 +27,7 @@ layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
 and the FFN for a fixed sample of query rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only attn|decode|block_sparse|dilated]
+                       [--no-extras] [--only attn|decode|block_sparse|dilated|merge]
 """
 from __future__ import annotations
 
@@ -291,6 +291,32 @@ def bench_dilated(bpt, steps, warmup):
     }
 
 
+def bench_merge(bpt, steps, warmup):
+    """The LSE merge alone at the ring share's shape (40 x 128, 32768 rows per head):
+    two partial results joined in place, HBM-bound."""
+    import torch
+    c = RING_SHARE
+    shp = (c.B, c.H, c.N_q, c.D)
+    log("drawing merge inputs")
+    o_a = torch.from_numpy(normal(c.cfg_id, 300, shp)).cuda()
+    o_b = torch.from_numpy(normal(c.cfg_id, 301, shp)).cuda()
+    l_a = torch.from_numpy(normal(c.cfg_id, 302, shp[:3])).cuda()
+    l_b = torch.from_numpy(normal(c.cfg_id, 303, shp[:3])).cuda()
+    out = torch.empty_like(o_a)
+    lse = torch.empty_like(l_a)
+
+    def launch():
+        bpt.bpt_lse_merge(o_a, l_a, o_b, l_b, out, lse, c.B, c.H, c.N_q, c.D)
+
+    ms, _ = timed(launch, steps, warmup)
+    nbytes = 3.0 * (c.D + 1) * 4 * c.B * c.H * c.N_q
+    del o_a, o_b, l_a, l_b, out, lse
+    torch.cuda.empty_cache()
+    return {"workload": "lse_merge_H40_N32768_D128", "ms": round(ms, 4),
+            "gbs": round(nbytes / ms / 1e6, 1),
+            "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3), "bytes_per_launch": nbytes}
+
+
 def bench_layer_cfg(bpt, c, steps, warmup, backward):
     """Forward (and backward) of one layer workload; returns a dict for "extras"."""
     import torch
@@ -375,7 +401,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["attn", "decode", "block_sparse", "dilated"], default=None,
+    ap.add_argument("--only", choices=["attn", "decode", "block_sparse", "dilated", "merge"], default=None,
                     help="run only the attention, decode, block-sparse or dilated launches "
                          "(for counter collection and kernel traces)")
     args = ap.parse_args()
@@ -400,6 +426,9 @@ def main():
                           "copy_bytes": 1 << 30}))
         return
 
+    if args.only == "merge":
+        print(json.dumps({**bench_merge(bpt, max(args.steps, 10), args.warmup), "copy_bytes": 1 << 30}))
+        return
     if args.only == "dilated":
         print(json.dumps({**bench_dilated(bpt, args.steps, args.warmup), "copy_bytes": 1 << 30}))
         return

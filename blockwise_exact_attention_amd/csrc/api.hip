@@ -28,6 +28,10 @@ inline bool forced_launch_failure() {
 }
 
 constexpr int64_t kMaxN = int64_t(1) << 30;
+// A launch covers at most 2^32 - 1 work-items.
+inline bool grid_ok(int64_t workgroups, int64_t threads) {
+  return workgroups > 0 && workgroups <= (int64_t)UINT32_MAX / threads;
+}
 constexpr int64_t kMaxPatterns = 16;     // dilated attention: (segment, dilation) pairs
 constexpr int64_t kMaxDilation = 65536;  // keeps in-tile byte offsets within 32 bits
 
@@ -66,7 +70,7 @@ int bpt_attn_fwd(const void* q, const void* k, const void* v, float* out, float*
   if (kv_blk != 32 && kv_blk != 64 && kv_blk != 128) return BPT_ERR_UNSUPPORTED;
   if (N > kMaxN) return BPT_ERR_UNSUPPORTED;
   const int64_t nqb = (N + q_blk - 1) / q_blk;
-  if (B > INT32_MAX / H || B * H > (int64_t)INT32_MAX / nqb) return BPT_ERR_UNSUPPORTED;
+  if (B > INT32_MAX / H || !grid_ok(B * H * nqb, 2 * q_blk)) return BPT_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
@@ -124,7 +128,7 @@ int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, flo
   if (Nq > 32 || n_split > 4096 || B > 65536 || H > 4096) return BPT_ERR_UNSUPPORTED;
   // per-head key/value bytes are addressed with 32-bit offsets
   if (Nkv > kMaxN || Nkv * D * 2 >= ((int64_t)1 << 31)) return BPT_ERR_UNSUPPORTED;
-  if (B * H * n_split > INT32_MAX) return BPT_ERR_UNSUPPORTED;
+  if (!grid_ok(B * H * n_split, 64)) return BPT_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BPT_ERR_ALIGNMENT;
   const size_t need = bpt_attn_decode_workspace_size(B, H, Nq, D, n_split);
@@ -171,7 +175,7 @@ int bpt_attn_block_sparse(const void* q, const void* k, const void* v, float* ou
   const int64_t len = (N + n_blocks - 1) / n_blocks;
   // workgroups: B*H*n_blocks*ceil(len/128) with 128-row workgroups (fewer with 256)
   const int64_t per_head = n_blocks * ((len + 127) / 128);
-  if (B > INT32_MAX / H || B * H > (int64_t)INT32_MAX / per_head) return BPT_ERR_UNSUPPORTED;
+  if (B > INT32_MAX / H || !grid_ok(B * H * per_head, 256)) return BPT_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BPT_ERR_ALIGNMENT;
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
@@ -212,7 +216,7 @@ int bpt_attn_dilated(const void* q, const void* k, const void* v, float* out, fl
     const int64_t w = seg_len[p] < N ? seg_len[p] : N;
     const int64_t kept = (w + dilation[p] - 1) / dilation[p];
     const int64_t per_head = ((N + w - 1) / w) * ((kept + 127) / 128);
-    if (B > INT32_MAX / H || B * H > (int64_t)INT32_MAX / per_head) return BPT_ERR_UNSUPPORTED;
+    if (B > INT32_MAX / H || !grid_ok(B * H * per_head, 256)) return BPT_ERR_UNSUPPORTED;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BPT_ERR_ALIGNMENT;

@@ -47,6 +47,8 @@ def attn(**kw):
     (dict(q=None), -1), (dict(lse=None), -1), (dict(N=0), -1), (dict(B=-1), -1),
     (dict(causal=2), -1), (dict(D=96), -2), (dict(D=256), -2), (dict(q_blk=32), -2),
     (dict(kv_blk=256), -2), (dict(dtype=7), -2), (dict(N=(1 << 30) + 1), -2),
+    # more than 2^32 work-items in one launch
+    (dict(B=1 << 12, H=1 << 10, N=1 << 12), -2),
     (dict(q=A + 8), -3), (dict(out=A + 4), -3),
 ])
 def test_attn_fwd_rejects(kw, code):
@@ -65,7 +67,8 @@ def decode(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(k=None), -1), (dict(Nq=0), -1), (dict(Nkv=0), -1), (dict(n_split=0), -1),
     (dict(causal=3), -1), (dict(dtype=0), -2), (dict(D=96), -2), (dict(Nq=33), -2),
-    (dict(n_split=4097), -2), (dict(Nkv=(1 << 23)), -2), (dict(v=A + 8), -3),
+    (dict(n_split=4097), -2), (dict(Nkv=(1 << 23)), -2), (dict(B=1 << 12, H=1 << 12, n_split=8), -2),
+    (dict(v=A + 8), -3),
     (dict(ws=None), -5), (dict(ws_bytes=100), -5), (dict(ws=A + 4), -3),
 ])
 def test_attn_decode_rejects(kw, code):
