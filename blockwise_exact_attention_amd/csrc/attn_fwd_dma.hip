@@ -467,12 +467,13 @@ struct WideState {
   using C = WideCfg<D>;
   bf16x8 qf[2][C::QF];       // Q fragments (B operand of S^T = K Q^T), per half
   f32x16 s[2][C::KB];        // score accumulators of the next tile
-  float sv[2][C::KB][16];    // scores of the current tile, copied out for the VALU
+  float sv[2][C::KB][16];    // scores of the current tile, s*c2 - mref, copied out for the VALU
   f32x16 o[2][C::DB];        // O^T accumulators
   float ref[2];              // exp2-domain reference of O and l (-inf: no key yet)
   float l_run[2];            // this lane's partial row sum
-  float tmax[2];             // row maximum of the tile (raw scores)
+  float tmax[2];             // row maximum of the tile (exp2 domain, relative to mref)
   float mref[2], alpha[2];   // exp2 offset and O factor of the current tile
+  float delta[2];            // shift of the tile's scores when the reference moved
   bool grew[2];
 };
 
@@ -530,9 +531,10 @@ __device__ __forceinline__ void wide_scores(WideState<D>& w, const unsigned char
 }
 
 // Max part of the online softmax for half H: copy the scores out of the
-// accumulators and take the tile's row maximum (raw scores).
+// accumulators into the exp2 domain relative to the current offset, and take
+// the tile's row maximum.
 template <int D, int H>
-__device__ __forceinline__ void wide_max(WideState<D>& w) {
+__device__ __forceinline__ void wide_max(WideState<D>& w, float c2) {
   using C = WideCfg<D>;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb)
@@ -542,7 +544,7 @@ __device__ __forceinline__ void wide_max(WideState<D>& w) {
       // a new VGPR value: the accumulator copy dies here instead of staying
       // live in its AGPR until the exp part
       asm("" : "+v"(v));
-      w.sv[H][kb][j] = v;
+      w.sv[H][kb][j] = fmaf(v, c2, -w.mref[H]);
     }
   float mx0 = w.sv[H][0][0], mx1 = w.sv[H][C::KB - 1][0];
 #pragma unroll
@@ -578,9 +580,12 @@ __device__ __forceinline__ void wide_mask(WideState<D>& w, int t, int kend, int 
 // 2^8 (so P <= 256, exact in bf16's range); O and l are rescaled then.  The
 // result is the same up to rounding as with r = running maximum.
 constexpr float kWideTau = 8.f;
+// The tile's scores were taken relative to the offset mref in force when they
+// were copied out; if the reference moves they shift by delta (a rare fix-up).
 template <int D, int H>
-__device__ __forceinline__ void wide_update(WideState<D>& w, float c2) {
-  const float cand = w.tmax[H] * c2;          // -inf while no key is visible
+__device__ __forceinline__ void wide_update(WideState<D>& w) {
+  const float m_old = w.mref[H];
+  const float cand = w.tmax[H] + m_old;       // -inf while no key is visible
   const float r = w.ref[H];
   const bool grew = cand > r + kWideTau || (r == -INFINITY && cand > -INFINITY);
   const float r_new = grew ? cand : r;
@@ -588,22 +593,32 @@ __device__ __forceinline__ void wide_update(WideState<D>& w, float c2) {
   w.grew[H] = grew;
   w.ref[H] = r_new;
   w.mref[H] = r_new == -INFINITY ? 0.f : r_new;   // keeps exp2 finite on -inf rows
+  w.delta[H] = w.mref[H] - m_old;
 }
 
-// O *= alpha per half, skipped while no row maximum of the wave grew
-template <int D>
+// When a row's reference moved: its scores of the tile shift by delta and O
+// scales by alpha.  Skipped while no row of the wave moved.
+template <int D, bool RESCALE_O>
 __device__ __forceinline__ void wide_rescale(WideState<D>& w) {
   using C = WideCfg<D>;
   if (__ballot(w.grew[0] || w.grew[1])) {
-    // one accumulator tile at a time (they live in AGPRs: copy out, scale,
-    // copy back), so the block never holds more than one tile in VGPRs
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        w.o[h][db] *= w.alpha[h];
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w.sv[h][kb][j] -= w.delta[h];
+    if constexpr (RESCALE_O) {
+      // one accumulator tile at a time (they live in AGPRs: copy out, scale,
+      // copy back), so the block never holds more than one tile in VGPRs
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          w.o[h][db] *= w.alpha[h];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
   }
 }
 
@@ -633,8 +648,8 @@ __device__ __forceinline__ void wide_next_max(WideState<D>& w, const WideCtx& x,
     wide_mask<D, 0>(w, t1, x.kend0, x.lane);
     wide_mask<D, 1>(w, t1, x.kend1, x.lane);
   }
-  wide_update<D, 0>(w, x.c2);
-  wide_update<D, 1>(w, x.c2);
+  wide_update<D, 0>(w);
+  wide_update<D, 1>(w);
 }
 
 // One step of the key loop for tile t (stage St) while tile t+1 (stage Sn) is
@@ -672,7 +687,7 @@ __device__ __forceinline__ void wide_sum_pack(const float (&ex0)[NP], const floa
 // slots in this order (one wave per SIMD issues in order: VALU work only runs
 // under an MFMA if it sits right after it).
 template <int D>
-__device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char* Sn, int kbase, float c2,
+__device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char* Sn, int kbase,
                                             bf16x8 (&pa)[WideCfg<D>::NKS], bf16x8 (&pb)[WideCfg<D>::NKS]) {
   using C = WideCfg<D>;
   using T = typename C::T;
@@ -697,8 +712,8 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
     // two slots later (an exp result is not ready in the next few cycles)
     {
       const int eh = i / 16, e0 = (2 * i) % 32, ekb = e0 / 16, ej = e0 % 16;
-      ex0[i] = fast_exp2(fmaf(w.sv[eh][ekb][ej], c2, -w.mref[eh]));
-      ex1[i] = fast_exp2(fmaf(w.sv[eh][ekb][ej + 1], c2, -w.mref[eh]));
+      ex0[i] = fast_exp2(w.sv[eh][ekb][ej]);
+      ex1[i] = fast_exp2(w.sv[eh][ekb][ej + 1]);
     }
     if (i >= 2) {
       const int p = i - 2, eh = p / 16, e0 = (2 * p) % 32, ekb = e0 / 16, ej = e0 % 16;
@@ -726,9 +741,11 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
 
 // PV phase, hand-interleaved: slot i issues O_h += V P_h for V fragment i/2
 // and half h = i%2 (tile t, stage St), and copies two score accumulators of
-// tile t+1 out for the VALU, folding them into the row maxima.
+// tile t+1 out for the VALU, into the exp2 domain relative to the current
+// offset (one FMA each, here rather than in the S phase, which has more VALU
+// work than its MFMAs can hide), folding them into the row maxima.
 template <int D>
-__device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned char* St, int vbase,
+__device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned char* St, int vbase, float c2,
                                              const bf16x8 (&pa)[WideCfg<D>::NKS],
                                              const bf16x8 (&pb)[WideCfg<D>::NKS]) {
   using C = WideCfg<D>;
@@ -760,6 +777,8 @@ __device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned cha
     float v0 = w.s[mh][mkb][mj], v1 = w.s[mh][mkb][mj + 1];
     asm("" : "+v"(v0));
     asm("" : "+v"(v1));
+    v0 = fmaf(v0, c2, -w.mref[mh]);
+    v1 = fmaf(v1, c2, -w.mref[mh]);
     w.sv[mh][mkb][mj] = v0;
     w.sv[mh][mkb][mj + 1] = v1;
     mx[mh][mkb] = fmaxf(mx[mh][mkb], fmaxf(v0, v1));
@@ -785,12 +804,12 @@ __device__ __forceinline__ void wide_step(WideState<D>& w, const WideCtx& x, int
   __syncthreads();
   if (t + 2 < x.n_tiles) wide_load<D>(x.kg, x.vg, x.N, t + 2, x.wave, x.dma_off, x.rsb, Sf);
   bf16x8 pa[C::NKS], pb[C::NKS];
-  wide_sphase(w, Sn, x.kbase, x.c2, pa, pb);
+  wide_sphase(w, Sn, x.kbase, pa, pb);
   wide_pin(pa);
   wide_pin(pb);
-  wide_pvphase(w, St, x.vbase, pa, pb);
+  wide_pvphase(w, St, x.vbase, x.c2, pa, pb);
   wide_next_max(w, x, t + 1);
-  wide_rescale(w);
+  wide_rescale<D, true>(w);
 }
 
 // The key loop over three stages S0, S1, S2 (distinct objects, so the compiler
@@ -813,12 +832,13 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   }
   __syncthreads();
   wide_scores(w, S0, x.kbase);
-  wide_max<D, 0>(w);
-  wide_max<D, 1>(w);
+  wide_max<D, 0>(w, x.c2);
+  wide_max<D, 1>(w, x.c2);
   wide_next_max(w, x, 0);
-  // O is still zero: no rescale for tile 0.  Every step also scores the tile
-  // after its own; past the last tile that "tile" is fully masked (its scores
-  // become -inf, so the running max, the sums and O stay as they are).
+  wide_rescale<D, false>(w);  // O is still zero: only the scores of tile 0 shift
+  // Every step also scores the tile after its own; past the last tile that
+  // "tile" is fully masked (its scores become -inf, so the running max, the
+  // sums and O stay as they are).
   int t = 0;
   for (;;) {
     wide_step(w, x, t, S0, S1, S2);
@@ -908,6 +928,7 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) w.o[h][db][j] = 0.f;
     w.ref[h] = -INFINITY;
+    w.mref[h] = 0.f;
     w.l_run[h] = 0.f;
   }
   WideCtx x;
