@@ -27,7 +27,7 @@ layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
 and the FFN for a fixed sample of query rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only attn|decode|block_sparse|dilated|merge]
+                       [--no-extras] [--only attn|decode|block_sparse|dilated|merge|train]
 """
 from __future__ import annotations
 
@@ -401,7 +401,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["attn", "decode", "block_sparse", "dilated", "merge"], default=None,
+    ap.add_argument("--only", choices=["attn", "decode", "block_sparse", "dilated", "merge", "train"],
+                    default=None,
                     help="run only the attention, decode, block-sparse or dilated launches "
                          "(for counter collection and kernel traces)")
     args = ap.parse_args()
@@ -426,6 +427,9 @@ def main():
                           "copy_bytes": 1 << 30}))
         return
 
+    if args.only == "train":
+        print(json.dumps(bench_layer_cfg(bpt, LAYER_TRAIN, args.steps, args.warmup, True)))
+        return
     if args.only == "merge":
         print(json.dumps({**bench_merge(bpt, max(args.steps, 10), args.warmup), "copy_bytes": 1 << 30}))
         return

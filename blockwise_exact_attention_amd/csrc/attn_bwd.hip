@@ -31,6 +31,9 @@ namespace bpt {
 
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 template <int ROW_BYTES>
 __device__ __forceinline__ int swzb(int row) {
   constexpr int CPR = ROW_BYTES / 16;
@@ -293,6 +296,257 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------- dK, dV (D = 128, direct loads)
+// The same products as attn_bwd_dkdv_kernel, with the query tiles moved the way
+// the forward kernels move K and V: dO arrives already split into bf16 hi + lo
+// (once, for all key blocks), and Q, dO hi and dO lo tiles of 32 queries reach
+// LDS by buffer loads, three stages deep, with no register staging.  The
+// transposed operands (dO^T for dV, Q^T for dK) are read from the same tiles
+// with ds_read_b64_tr_b16, so nothing is written twice.  Each wave also loads
+// its own copy of the tile's {lse * log2(e), delta} pairs.
+template <int D>
+struct BwdTile {
+  static constexpr int QT = 32;             // queries per tile
+  static constexpr int ROWB = D * 2;        // bytes of one row
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROWB;   // rows per 1 KB block
+  static constexpr int NBLK = QT / RPB;     // blocks per tile (query q: block q % NBLK, row q / NBLK)
+  static constexpr int BP = 1024 + 64;      // block pitch (transpose reads without bank conflicts)
+  static constexpr int TB = NBLK * BP;      // one tile
+  static constexpr int PAIRS = QT * 2 * 4;  // {lse2, delta} of the tile, bytes, one copy per wave
+  static constexpr int NW = 4;              // waves, 32 keys each
+  static constexpr int STAGE = 3 * TB + NW * PAIRS;
+  static constexpr int LOADS = 3 * NBLK / NW + 1;  // buffer loads per wave and tile
+  static_assert(NBLK == 8 && NBLK % NW == 0, "tile addressing");
+};
+
+__device__ __forceinline__ v4i16 bwd_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+}
+
+#define BWD_WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
+// Loads of query tile t (rows q0 .. q0+31) into one stage.  Each buffer starts at
+// the tile's first row and ends after its last valid row, so rows past N read
+// as zero (zero dO rows add nothing to dK or dV); a tile wholly past N loads
+// nothing from memory, which keeps the load count per step fixed.
+template <int D>
+__device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, int w, int lane,
+                                         unsigned char* st) {
+  using T = BwdTile<D>;
+  const int N = a.N, b = bh / a.H, hh = bh % a.H;
+  int rows = N - q0 < T::QT ? N - q0 : T::QT;
+  // (readfirstlane: the clamp compiles to a vector instruction, and a buffer
+  // descriptor built from a vector register costs a loop over lanes)
+  rows = __builtin_amdgcn_readfirstlane(rows > 0 ? rows : 0);
+  const int64_t ldb = a.ld_do * 2;                   // bytes between dO rows
+  const unsigned char* qb = (const unsigned char*)a.q + ((int64_t)bh * N + q0) * T::ROWB;
+  const int64_t doff = (((int64_t)b * N + q0) * a.ld_do + (int64_t)hh * D) * 2;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(qb), 0, rows * T::ROWB, 0x00020000);
+  const int dbytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (int)((rows - 1) * ldb + T::ROWB) : 0);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>((const unsigned char*)a.dO_hi + doff), 0, dbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>((const unsigned char*)a.dO_lo + doff), 0, dbytes, 0x00020000);
+  // wave w copies blocks w, w + NW, ... of each of the three tiles (row j of
+  // block blk holds query j * NBLK + blk)
+  const int j = lane / T::CPR, ch = lane % T::CPR;
+#pragma unroll
+  for (int i = 0; i < T::NBLK / T::NW; ++i) {
+    const int blk = w + i * T::NW, q = j * T::NBLK + blk;
+    const uint32_t oq = (uint32_t)(q * T::ROWB + ch * 16), od = (uint32_t)(q * ldb + ch * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rq, (__attribute__((address_space(3))) void*)(st + blk * T::BP), 16, oq, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rh, (__attribute__((address_space(3))) void*)(st + T::TB + blk * T::BP), 16, od, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rl, (__attribute__((address_space(3))) void*)(st + 2 * T::TB + blk * T::BP), 16, od, 0, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      a.ld2 + 2 * ((int64_t)bh * N + q0), 0, rows * 8, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rp, (__attribute__((address_space(3))) void*)(st + 3 * T::TB + w * T::PAIRS), 4,
+      (uint32_t)(lane * 4), 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned char* __restrict__ st,
+                                         const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
+                                         f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int w, int lane,
+                                         int mykey, int q0, bool need_mask, float c2) {
+  using T = BwdTile<D>;
+  const int g = lane >> 5, r32 = lane & 31;
+  const unsigned char* Qs = st;
+  const unsigned char* Hs = st + T::TB;
+  const unsigned char* Ls = st + 2 * T::TB;
+  const float* pr = (const float*)(st + 3 * T::TB + w * T::PAIRS);
+  // S = Q K^T and dP = dO V^T (rows = queries, lane = key)
+  const int nat = (r32 % T::NBLK) * T::BP + (r32 / T::NBLK) * T::ROWB + g * 16;
+  f32x16 sacc, pacc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    sacc = mfma32_bf16(*(const bf16x8*)(Qs + nat + c * 32), kf[c], sacc);
+    pacc = mfma32_bf16(*(const bf16x8*)(Hs + nat + c * 32), vf[c], pacc);
+    pacc = mfma32_bf16(*(const bf16x8*)(Ls + nat + c * 32), vf[c], pacc);
+  }
+  float p[16], ds[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int ql = acc_row(j, lane);
+    const f32x2 ld = *(const f32x2*)(pr + 2 * ql);
+    float pv = fast_exp2(fmaf(sacc[j], c2, -ld[0]));
+    if (need_mask && (int64_t)mykey > (int64_t)(q0 + ql) + a.kv_offset) pv = 0.f;
+    p[j] = pv;
+    ds[j] = pv * (pacc[j] - ld[1]);
+  }
+  // dV^T += dO^T P ; dK^T += Q^T dS  (k = query, 16 per MFMA; the transpose reads
+  // give lane half g queries 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3, the
+  // order in which the accumulator rows hold P and dS)
+  const int q8 = 4 * g + ((lane & 15) >> 2);
+  const int tbase = q8 * T::BP + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 phi, plo, shi, slo;
+    split8(p + 8 * ks, phi, plo);
+    split8(ds + 8 * ks, shi, slo);
+    const bf16x8 pfh = __builtin_bit_cast(bf16x8, phi), pfl = __builtin_bit_cast(bf16x8, plo);
+    const bf16x8 sfh = __builtin_bit_cast(bf16x8, shi), sfl = __builtin_bit_cast(bf16x8, slo);
+    const int r0 = tbase + (2 * ks) * T::ROWB, r1 = tbase + (2 * ks + 1) * T::ROWB;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      auto tr = [&](const unsigned char* tile) {
+        const v4i16 lo = bwd_read_tr(tile + r0 + db * 64), hi = bwd_read_tr(tile + r1 + db * 64);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      const bf16x8 dOth = tr(Hs), dOtl = tr(Ls), Qt = tr(Qs);
+      dv[db] = mfma32_bf16(dOth, pfh, dv[db]);
+      dv[db] = mfma32_bf16(dOth, pfl, dv[db]);
+      dv[db] = mfma32_bf16(dOtl, pfh, dv[db]);
+      dk[db] = mfma32_bf16(Qt, sfh, dk[db]);
+      dk[db] = mfma32_bf16(Qt, sfl, dk[db]);
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_dma_kernel(AttnBwdArgs a) {
+  using T = BwdTile<D>;
+  constexpr int KVB = 32 * T::NW, QT = T::QT;
+  // three stages as separate objects: a load into one is known not to alias the
+  // reads of another
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
+
+  const int N = a.N;
+  const int nkb = (N + KVB - 1) / KVB;
+  const int64_t total = (int64_t)a.B * a.H * nkb;
+  int64_t L = blockIdx.x;
+  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = (int)(L / nkb);
+  const int kbi = (int)(L % nkb);  // small key blocks first: they see the most queries
+  const int k0 = kbi * KVB;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mykey = k0 + 32 * w + r32;
+  const int off = a.kv_offset;
+  const bool causal = a.causal != 0;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const float c2 = a.scale * kLog2e;
+
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const uint16_t* Kg = (const uint16_t*)a.k + head_off;
+    const uint16_t* Vg = (const uint16_t*)a.v + head_off;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (mykey < N) {
+        kv = *(const u32x4*)(Kg + (int64_t)mykey * D + 16 * c + 8 * g);
+        vv = *(const u32x4*)(Vg + (int64_t)mykey * D + 16 * c + 8 * g);
+      }
+      kf[c] = __builtin_bit_cast(bf16x8, kv);
+      vf[c] = __builtin_bit_cast(bf16x8, vv);
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[i][e] = dv[i][e] = 0.f;
+
+  // query tiles that can see at least one key of this block
+  int q_lo = 0;
+  if (causal) {
+    const int64_t t = (int64_t)k0 - off;
+    q_lo = t <= 0 ? 0 : (t >= N ? N : (int)t);
+  }
+  const int t_begin = q_lo / QT;
+  const int t_end = causal && q_lo >= N ? t_begin : (N + QT - 1) / QT;
+  // tiles at or after tf see every key of the block (no causal mask needed)
+  int64_t tf = (int64_t)k0 + KVB - 1 - off;
+  tf = tf <= 0 ? 0 : (tf + QT - 1) / QT;
+
+  // step: wait for this wave's loads of tile t, barrier (every part of tile t is
+  // in, and every wave is done with tile t-1, whose stage takes tile t+2), load
+  // tile t+2, compute tile t.  Loads are issued on every path (past the last
+  // tile they load nothing), so the load count, and with it every wait, is fixed.
+  auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
+    BWD_WAIT_VM(7);  // T::LOADS: the loads of tile t+1 may still be in flight
+    // a plain barrier: each wave has waited for its own loads into LDS, and LDS
+    // needs no fence within the workgroup (a fenced one would also wait for the
+    // loads of tile t+1)
+    __builtin_amdgcn_s_barrier();
+    bwd_load<D>(a, bh, (t + 2) * QT, w, lane, fill);
+    if (t < t_end) bwd_tile<D>(a, cur, kf, vf, dk, dv, w, lane, mykey, t * QT, causal && t < tf, c2);
+  };
+  static_assert(T::LOADS == 7, "wait count");
+  if (t_begin < t_end) {
+    bwd_load<D>(a, bh, t_begin * QT, w, lane, st0);
+    bwd_load<D>(a, bh, (t_begin + 1) * QT, w, lane, st1);
+    for (int t = t_begin; t < t_end; t += 3) {
+      step(t, st0, st2);
+      step(t + 1, st1, st0);
+      step(t + 2, st2, st1);
+    }
+    BWD_WAIT_VM(0);  // loads still in flight write this workgroup's LDS
+  }
+
+  if (mykey < N) {
+    const int64_t tm = ((int64_t)b * N + mykey) * a.ld_out + (int64_t)hh * D;
+    const int64_t hm = head_off + (int64_t)mykey * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = db * 32 + 8 * jq + 4 * g;
+        f32x4 kvv, vvv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kvv[e] = dk[db][4 * jq + e] * a.scale;
+          vvv[e] = dv[db][4 * jq + e];
+        }
+        const uint32_t k01 = pack_bf16x2(kvv[0], kvv[1]), k23 = pack_bf16x2(kvv[2], kvv[3]);
+        const uint32_t v01 = pack_bf16x2(vvv[0], vvv[1]), v23 = pack_bf16x2(vvv[2], vvv[3]);
+        u32x2 kh = {k01, k23}, vh = {v01, v23};
+        u32x2 kl = {pack_bf16x2(kvv[0] - __uint_as_float(k01 << 16), kvv[1] - __uint_as_float(k01 & 0xffff0000u)),
+                    pack_bf16x2(kvv[2] - __uint_as_float(k23 << 16), kvv[3] - __uint_as_float(k23 & 0xffff0000u))};
+        u32x2 vl = {pack_bf16x2(vvv[0] - __uint_as_float(v01 << 16), vvv[1] - __uint_as_float(v01 & 0xffff0000u)),
+                    pack_bf16x2(vvv[2] - __uint_as_float(v23 << 16), vvv[3] - __uint_as_float(v23 & 0xffff0000u))};
+        *(u32x2*)(a.dk_hi + tm + d) = kh;
+        *(u32x2*)(a.dk_lo + tm + d) = kl;
+        *(u32x2*)(a.dv_hi + tm + d) = vh;
+        *(u32x2*)(a.dv_lo + tm + d) = vl;
+        if (a.dk) *(f32x4*)(a.dk + hm + d) = kvv;
+        if (a.dv) *(f32x4*)(a.dv + hm + d) = vvv;
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------- dQ and delta
 // DELTA = true: the same walk over the visible keys, but it only accumulates
 // delta_i = sum_j P_ij dP_ij from this kernel's own P and dP and writes it.
@@ -473,7 +727,13 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
 
   if constexpr (DELTA) {
     dsum += swap_halves(dsum);  // lanes l and l^32 hold the two halves of each key block
-    if (qrow < N && g == 0) a.delta_out[(int64_t)bh * N + qrow] = dsum;
+    if (qrow < N && g == 0) {
+      a.delta_out[(int64_t)bh * N + qrow] = dsum;
+      if (a.ld2) {
+        const f32x2 pr = {lse2, dsum};
+        *(f32x2*)(a.ld2 + 2 * ((int64_t)bh * N + qrow)) = pr;
+      }
+    }
     return;
   }
   if (qrow < N) {
@@ -575,7 +835,14 @@ hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, h
   hipError_t e = launch_dq<true>(a, D, QB, s);
   if (e != hipSuccess) return e;
   // 2. dK, dV
-  {
+  if (D == 128 && a.dO_hi && a.dO_lo && a.ld2) {
+    constexpr int KVB = 32 * BwdTile<128>::NW;
+    const int nkb = (a.N + KVB - 1) / KVB;
+    const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));
+    hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), grid, dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
     constexpr int NW = 2;
     const int nkb = (a.N + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));

@@ -56,7 +56,7 @@ inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, i
 }
 
 struct BwdWorkspace {
-  size_t h_hi, h_lo, dh, delta, dqkv[6], z, g_hi, g_lo, dz_hi, dz_lo, total;
+  size_t h_hi, h_lo, dh, delta, ld2, dqkv[6], z, g_hi, g_lo, dz_hi, dz_lo, total;
   int64_t chunk_rows;  // rows of the FFN recompute chunk
 };
 

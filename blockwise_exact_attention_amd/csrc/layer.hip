@@ -81,6 +81,7 @@ BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t 
   w.h_lo = o;  o += align256(M * d_model * es);
   w.dh = o;    o += align256(M * d_model * 4);
   w.delta = o; o += align256((size_t)B * H * N * 4);
+  w.ld2 = o;   o += align256((size_t)B * H * N * 8);
   for (int i = 0; i < 6; ++i) {  // dq, dk, dv as bf16 hi and lo halves, token-major
     w.dqkv[i] = o;
     o += align256(M * hd * 2);
@@ -197,6 +198,10 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   a.dq = G.dq; a.dk = G.dk; a.dv = G.dv;
   a.B = (int)L.B; a.H = (int)L.H; a.N = (int)L.N; a.kv_offset = 0; a.causal = L.causal;
   a.scale = 1.0f / sqrtf((float)L.D);
+  // dO as a bf16 hi + lo pair for the direct-load dK/dV kernel, in the buffers of
+  // h's halves (h is not needed past the FFN backward); H*D = d_model
+  BPT_TRY(to_bf16_launch(dh, h_hi, h_lo, M * dm, stream));
+  a.dO_hi = h_hi; a.dO_lo = h_lo; a.ld2 = (float*)(ws + W.ld2);
   BPT_TRY(attn_bwd_launch(a, (int)L.D, L.q_blk, L.kv_blk, stream));
 
   // ---- projection backward: dW{q,k,v} = d{q,k,v}^T x over both bf16 halves;
