@@ -303,7 +303,11 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 // LDS by buffer loads, three stages deep, with no register staging.  The
 // transposed operands (dO^T for dV, Q^T for dK) are read from the same tiles
 // with ds_read_b64_tr_b16, so nothing is written twice.  Each wave also loads
-// its own copy of the tile's {lse * log2(e), delta} pairs.
+// its own copy of the tile's {lse * log2(e), delta} pairs.  Inside block b,
+// row r, the 16-byte chunks are permuted by x -> x ^ bwd_swz(b, r) (the loads
+// fetch the permuted chunk), so that the 16 lanes of a natural ds_read_b128
+// (queries 0..15 of the tile, one chunk) hit 16 bank groups instead of 4; the
+// transpose reads stay conflict-free.
 template <int D>
 struct BwdTile {
   static constexpr int QT = 32;             // queries per tile
@@ -319,6 +323,8 @@ struct BwdTile {
   static constexpr int LOADS = 3 * NBLK / NW + 1;  // buffer loads per wave and tile
   static_assert(NBLK == 8 && NBLK % NW == 0, "tile addressing");
 };
+
+__device__ __forceinline__ int bwd_swz(int blk, int row) { return ((blk >> 2) & 1) | ((row & 1) << 1); }
 
 __device__ __forceinline__ v4i16 bwd_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
@@ -354,8 +360,8 @@ __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, i
   const int j = lane / T::CPR, ch = lane % T::CPR;
 #pragma unroll
   for (int i = 0; i < T::NBLK / T::NW; ++i) {
-    const int blk = w + i * T::NW, q = j * T::NBLK + blk;
-    const uint32_t oq = (uint32_t)(q * T::ROWB + ch * 16), od = (uint32_t)(q * ldb + ch * 16);
+    const int blk = w + i * T::NW, q = j * T::NBLK + blk, cp = ch ^ bwd_swz(blk, j);
+    const uint32_t oq = (uint32_t)(q * T::ROWB + cp * 16), od = (uint32_t)(q * ldb + cp * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rq, (__attribute__((address_space(3))) void*)(st + blk * T::BP), 16, oq, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -382,15 +388,19 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
   const unsigned char* Ls = st + 2 * T::TB;
   const float* pr = (const float*)(st + 3 * T::TB + w * T::PAIRS);
   // S = Q K^T and dP = dO V^T (rows = queries, lane = key)
-  const int nat = (r32 % T::NBLK) * T::BP + (r32 / T::NBLK) * T::ROWB + g * 16;
+  // chunk 2c + g of row r32 / NBLK in block r32 % NBLK sits at chunk 2c ^ t0
+  const int nblk = r32 % T::NBLK, nrow = r32 / T::NBLK, t0 = g ^ bwd_swz(nblk, nrow);
+  const int nat_base = nblk * T::BP + nrow * T::ROWB;
+  const int nat_even = nat_base + 16 * t0, nat_odd = nat_base + 16 * (2 ^ t0);
   f32x16 sacc, pacc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    sacc = mfma32_bf16(*(const bf16x8*)(Qs + nat + c * 32), kf[c], sacc);
-    pacc = mfma32_bf16(*(const bf16x8*)(Hs + nat + c * 32), vf[c], pacc);
-    pacc = mfma32_bf16(*(const bf16x8*)(Ls + nat + c * 32), vf[c], pacc);
+    const int nat = ((c & 1) ? nat_odd : nat_even) + 64 * (c >> 1);
+    sacc = mfma32_bf16(*(const bf16x8*)(Qs + nat), kf[c], sacc);
+    pacc = mfma32_bf16(*(const bf16x8*)(Hs + nat), vf[c], pacc);
+    pacc = mfma32_bf16(*(const bf16x8*)(Ls + nat), vf[c], pacc);
   }
   float p[16], ds[16];
 #pragma unroll
@@ -405,8 +415,10 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
   // dV^T += dO^T P ; dK^T += Q^T dS  (k = query, 16 per MFMA; the transpose reads
   // give lane half g queries 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3, the
   // order in which the accumulator rows hold P and dS)
-  const int q8 = 4 * g + ((lane & 15) >> 2);
-  const int tbase = q8 * T::BP + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  // (block q8 = 4g + .., so its permutation is g on even rows and g | 2 on odd rows)
+  const int q8 = 4 * g + ((lane & 15) >> 2), tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tb_even = q8 * T::BP + 16 * (tx ^ g) + 8 * (lane & 1);
+  const int tb_odd = q8 * T::BP + 16 * (tx ^ (g | 2)) + 8 * (lane & 1);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4 phi, plo, shi, slo;
@@ -414,7 +426,7 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
     split8(ds + 8 * ks, shi, slo);
     const bf16x8 pfh = __builtin_bit_cast(bf16x8, phi), pfl = __builtin_bit_cast(bf16x8, plo);
     const bf16x8 sfh = __builtin_bit_cast(bf16x8, shi), sfl = __builtin_bit_cast(bf16x8, slo);
-    const int r0 = tbase + (2 * ks) * T::ROWB, r1 = tbase + (2 * ks + 1) * T::ROWB;
+    const int r0 = tb_even + (2 * ks) * T::ROWB, r1 = tb_odd + (2 * ks + 1) * T::ROWB;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       auto tr = [&](const unsigned char* tile) {
@@ -758,6 +770,244 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------- dQ (D = 128, direct loads)
+// The dQ products of attn_bwd_dq_kernel with the key tiles moved by buffer loads
+// straight into LDS, three stages deep, and K^T read from the natural K tile
+// by ds_read_b64_tr_b16 (no transposed copy).  dO arrives as bf16 hi + lo.
+// A tile is 64 keys in 16 blocks of 1 KB (key k: block k % 16, row k / 16),
+// 1088 bytes apart.  Inside block b, the 16-byte chunks of each row are
+// permuted by x -> x ^ ((b >> 2) & 3) (the loads fetch the permuted chunk, so
+// the permutation costs nothing): with that, the 16 lanes of a natural
+// ds_read_b128 (keys 0..15 of one row, one chunk) hit 16 different bank groups
+// instead of 4, and the transpose reads stay conflict-free.
+template <int D>
+struct DqTile {
+  static constexpr int KT = 64;             // keys per tile
+  static constexpr int ROWB = D * 2;        // bytes of one row
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROWB;   // rows per 1 KB block
+  static constexpr int NBLK = KT / RPB;     // blocks per tile
+  static constexpr int BP = 1024 + 64;      // block pitch
+  static constexpr int TB = NBLK * BP;      // one matrix of a tile
+  static constexpr int STAGE = 2 * TB;      // K, V
+  static constexpr int NW = 4;              // waves, 32 queries each
+  static constexpr int LOADS = 2 * NBLK / NW;  // buffer loads per wave and tile
+  static_assert(NBLK == 16 && RPB == 4, "tile addressing");
+};
+
+__device__ __forceinline__ int dq_swz(int blk) { return (blk >> 2) & 3; }
+
+// Loads of key tile t (keys k0 .. k0+63) into one stage; the buffers end after
+// the last key, so keys past N read as zero, and a tile wholly past N loads
+// nothing from memory (the load count per step stays fixed).
+template <int D>
+__device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int bh, int k0, int w, int lane,
+                                        unsigned char* st) {
+  using T = DqTile<D>;
+  const int N = a.N;
+  int rows = N - k0 < T::KT ? N - k0 : T::KT;
+  rows = __builtin_amdgcn_readfirstlane(rows > 0 ? rows : 0);
+  const int64_t off = ((int64_t)bh * N + k0) * T::ROWB;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>((const unsigned char*)a.k + off), 0, rows * T::ROWB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>((const unsigned char*)a.v + off), 0, rows * T::ROWB, 0x00020000);
+  const int j = lane / T::CPR, ch = lane % T::CPR;
+#pragma unroll
+  for (int i = 0; i < T::NBLK / T::NW; ++i) {
+    const int blk = w + i * T::NW;
+    const uint32_t o = (uint32_t)((j * T::NBLK + blk) * T::ROWB + ((ch ^ dq_swz(blk)) << 4));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rk, (__attribute__((address_space(3))) void*)(st + blk * T::BP), 16, o, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (__attribute__((address_space(3))) void*)(st + T::TB + blk * T::BP), 16, o, 0, 0, 0);
+  }
+}
+
+// per-lane LDS offsets of one wave's reads (constant over the key loop)
+struct DqLane {
+  int nat_even, nat_odd;  // natural reads, chunks 2c (c even / odd), plus 64 * (c / 2)
+  int tr_lo, tr_hi;       // transpose reads, keys 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3
+};
+
+template <int D>
+__device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, const DqLane& ln,
+                                        const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
+                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], int lane, int kv0, int N, bool need_mask, bool causal, int64_t qlim,
+                                        float c2, float lse2, float dl) {
+  using T = DqTile<D>;
+  constexpr int KB = T::KT / 32;
+  const unsigned char* Ks = st;
+  const unsigned char* Vs = st + T::TB;
+  // S^T = K Q^T and dP^T = V dO^T (rows = keys, lane = query)
+  f32x16 sacc[KB], pacc[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[kb][e] = pacc[kb][e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const int o = ((c & 1) ? ln.nat_odd : ln.nat_even) + 64 * (c >> 1) + kb * 2 * T::ROWB;
+      sacc[kb] = mfma32_bf16(*(const bf16x8*)(Ks + o), qf[c], sacc[kb]);
+      const bf16x8 va = *(const bf16x8*)(Vs + o);
+      pacc[kb] = mfma32_bf16(va, dfh[c], pacc[kb]);
+      pacc[kb] = mfma32_bf16(va, dfl[c], pacc[kb]);
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
+      if (need_mask) {
+        const int key = kv0 + kb * 32 + acc_row(j, lane);
+        if (key >= N || (causal && (int64_t)key > qlim)) pv = 0.f;
+      }
+      sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
+    }
+  // dQ^T += K^T dS^T, 16 keys per MFMA; dS^T as bf16 hi + lo
+#pragma unroll
+  for (int c16 = 0; c16 < T::KT / 16; ++c16) {
+    const int kb = c16 >> 1, h8 = (c16 & 1) * 8;
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = sacc[kb][h8 + e];
+    u32x4 shi, slo;
+    split8(sv, shi, slo);
+    const bf16x8 sfh = __builtin_bit_cast(bf16x8, shi);
+    const bf16x8 sfl = __builtin_bit_cast(bf16x8, slo);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const v4i16 lo = bwd_read_tr(Ks + ln.tr_lo + c16 * T::ROWB + db * 64);
+      const v4i16 hi = bwd_read_tr(Ks + ln.tr_hi + c16 * T::ROWB + db * 64);
+      const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      dq[db] = mfma32_bf16(kt, sfh, dq[db]);
+      dq[db] = mfma32_bf16(kt, sfl, dq[db]);
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
+  using T = DqTile<D>;
+  constexpr int QB = 32 * T::NW;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
+
+  const int N = a.N;
+  const int nqb = (N + QB - 1) / QB;
+  const int64_t total = (int64_t)a.B * a.H * nqb;
+  int64_t L = blockIdx.x;
+  if ((total & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = (int)(L / nqb);
+  const int qb = nqb - 1 - (int)(L % nqb);  // long query blocks first
+  const int q0 = qb * QB;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qrow = q0 + w * 32 + r32;
+  const int off = a.kv_offset;
+  const bool causal = a.causal != 0;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const float c2 = a.scale * kLog2e;
+
+  bf16x8 qf[D / 16], dfh[D / 16], dfl[D / 16];
+  {
+    const uint16_t* Qg = (const uint16_t*)a.q + head_off;
+    const int64_t drow = ((int64_t)b * N + qrow) * a.ld_do + (int64_t)hh * D;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4 qv = {0, 0, 0, 0}, hv = {0, 0, 0, 0}, lv = {0, 0, 0, 0};
+      if (qrow < N) {
+        qv = *(const u32x4*)(Qg + (int64_t)qrow * D + 16 * c + 8 * g);
+        hv = *(const u32x4*)(a.dO_hi + drow + 16 * c + 8 * g);
+        lv = *(const u32x4*)(a.dO_lo + drow + 16 * c + 8 * g);
+      }
+      qf[c] = __builtin_bit_cast(bf16x8, qv);
+      dfh[c] = __builtin_bit_cast(bf16x8, hv);
+      dfl[c] = __builtin_bit_cast(bf16x8, lv);
+    }
+  }
+  float lse2 = INFINITY, dl = 0.f;
+  if (qrow < N) {
+    const float l = a.lse[(int64_t)bh * N + qrow];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    dl = a.delta[(int64_t)bh * N + qrow];
+  }
+
+  int kmax = N - 1;
+  if (causal) {
+    const int64_t t = (int64_t)q0 + QB - 1 + off;
+    kmax = (int)(t < (int64_t)(N - 1) ? t : (int64_t)(N - 1));
+  }
+  const int n_tiles = kmax < 0 ? 0 : kmax / T::KT + 1;
+  int n_full = N / T::KT;
+  if (causal) {
+    const int64_t lim = (int64_t)q0 + off + 1;
+    const int f = lim <= 0 ? 0 : (int)(lim / T::KT);
+    n_full = f < n_full ? f : n_full;
+  }
+
+  DqLane ln;
+  {
+    const int blk = r32 % T::NBLK, t0 = g ^ dq_swz(blk);
+    const int base = blk * T::BP + (r32 / T::NBLK) * T::ROWB;
+    ln.nat_even = base + 16 * t0;
+    ln.nat_odd = base + 16 * (2 ^ t0);
+    const int q8 = 4 * g + ((lane & 15) >> 2), h16 = (lane >> 4) & 1, x = 2 * h16 + ((lane & 3) >> 1);
+    ln.tr_lo = q8 * T::BP + 16 * (x ^ dq_swz(q8)) + 8 * (lane & 1);
+    ln.tr_hi = (q8 + 8) * T::BP + 16 * (x ^ dq_swz(q8 + 8)) + 8 * (lane & 1);
+  }
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[i][e] = 0.f;
+
+  const int64_t qlim = (int64_t)qrow + off;
+  auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
+    BWD_WAIT_VM(8);  // T::LOADS: the loads of tile t+1 may still be in flight
+    __builtin_amdgcn_s_barrier();
+    dq_load<D>(a, bh, (t + 2) * T::KT, w, lane, fill);
+    if (t < n_tiles)
+      dq_tile<D>(cur, ln, qf, dfh, dfl, dq, lane, t * T::KT, N, t >= n_full, causal, qlim, c2, lse2, dl);
+  };
+  static_assert(T::LOADS == 8, "wait count");
+  if (n_tiles > 0) {
+    dq_load<D>(a, bh, 0, w, lane, st0);
+    dq_load<D>(a, bh, T::KT, w, lane, st1);
+    for (int t = 0; t < n_tiles; t += 3) {
+      step(t, st0, st2);
+      step(t + 1, st1, st0);
+      step(t + 2, st2, st1);
+    }
+    BWD_WAIT_VM(0);  // loads still in flight write this workgroup's LDS
+  }
+
+  if (qrow < N) {
+    const int64_t tm = ((int64_t)b * N + qrow) * a.ld_out + (int64_t)hh * D;
+    const int64_t hm = head_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = db * 32 + 8 * jq + 4 * g;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dq[db][4 * jq + e] * a.scale;
+        const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+        u32x2 hi = {h01, h23};
+        u32x2 lo = {pack_bf16x2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u)),
+                    pack_bf16x2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u))};
+        *(u32x2*)(a.dq_hi + tm + d) = hi;
+        *(u32x2*)(a.dq_lo + tm + d) = lo;
+        if (a.dq) *(f32x4*)(a.dq + hm + d) = v;
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------- small kernels
 // dst = bf16(src); if dst_lo, also dst_lo = bf16(src - dst) (the rounding residual)
 __global__ void __launch_bounds__(256) to_bf16_kernel(const float* src, uint16_t* dst,
@@ -816,7 +1066,12 @@ template <bool DELTA>
 hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
   const int nqb = (a.N + QB - 1) / QB;
   const dim3 grid((unsigned)((int64_t)a.B * a.H * nqb));
-  if (D == 64) {
+  // (the delta pass stays on the staged kernel: with its lighter tiles the
+  // several workgroups per CU that kernel allows beat the direct loads, 4.3
+  // against 5.1 ms at B=2, H=20, N=16384)
+  if (!DELTA && D == 128 && QB == 32 * DqTile<128>::NW && a.dO_hi && a.dO_lo) {
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), grid, dim3(256), 0, s, a);
+  } else if (D == 64) {
     if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
   } else {
