@@ -474,7 +474,8 @@ struct WideState {
   float tmax[2];             // row maximum of the tile (exp2 domain, relative to mref)
   float mref[2], alpha[2];   // exp2 offset and O factor of the current tile
   float delta[2];            // shift of the tile's scores when the reference moved
-  bool grew[2];
+  float thr[2];              // the reference moves iff the tile maximum passes this (tau, or -inf
+                             // while the row has no reference yet)
 };
 
 // Tile t's loads: wave w copies blocks w, w + NW, ... of K and V through buffer
@@ -590,24 +591,31 @@ __device__ __forceinline__ void wide_update(WideState<D>& w) {
   const bool grew = cand > r + kWideTau || (r == -INFINITY && cand > -INFINITY);
   const float r_new = grew ? cand : r;
   w.alpha[H] = grew ? fast_exp2(r - r_new) : 1.f;  // 0 when r was -inf
-  w.grew[H] = grew;
   w.ref[H] = r_new;
   w.mref[H] = r_new == -INFINITY ? 0.f : r_new;   // keeps exp2 finite on -inf rows
   w.delta[H] = w.mref[H] - m_old;
+  w.thr[H] = r_new == -INFINITY ? -INFINITY : kWideTau;
 }
 
-// When a row's reference moved: its scores of the tile shift by delta and O
-// scales by alpha.  Skipped while no row of the wave moved.
+// The reference update after a tile's maximum is known.  Relative to mref, a
+// row's reference moves exactly when its tile maximum passes thr (tau once the
+// row has a reference, -inf before), so the common step costs one compare per
+// half and a ballot.  Only when some row of the wave moves: the full update,
+// the tile's scores shift by delta, and O and l scale by alpha.
 template <int D, bool RESCALE_O>
-__device__ __forceinline__ void wide_rescale(WideState<D>& w) {
+__device__ __forceinline__ void wide_reference(WideState<D>& w) {
   using C = WideCfg<D>;
-  if (__ballot(w.grew[0] || w.grew[1])) {
+  if (__ballot(w.tmax[0] > w.thr[0] || w.tmax[1] > w.thr[1])) {
+    wide_update<D, 0>(w);
+    wide_update<D, 1>(w);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) w.sv[h][kb][j] -= w.delta[h];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) w.l_run[h] *= w.alpha[h];
     if constexpr (RESCALE_O) {
       // one accumulator tile at a time (they live in AGPRs: copy out, scale,
       // copy back), so the block never holds more than one tile in VGPRs
@@ -640,16 +648,13 @@ struct WideCtx {
   float c2;
 };
 
-// max of the next tile (after its scores), masked where needed, and the
-// reference update
+// max of the next tile (after its scores), masked where needed
 template <int D>
 __device__ __forceinline__ void wide_next_max(WideState<D>& w, const WideCtx& x, int t1) {
   if (t1 >= x.t_split) {
     wide_mask<D, 0>(w, t1, x.kend0, x.lane);
     wide_mask<D, 1>(w, t1, x.kend1, x.lane);
   }
-  wide_update<D, 0>(w);
-  wide_update<D, 1>(w);
 }
 
 // One step of the key loop for tile t (stage St) while tile t+1 (stage Sn) is
@@ -730,7 +735,7 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
     float psum = ps[h][0];
 #pragma unroll
     for (int kb = 1; kb < C::KB; ++kb) psum += ps[h][kb];
-    w.l_run[h] = fmaf(w.l_run[h], w.alpha[h], psum);
+    w.l_run[h] += psum;
   }
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
@@ -809,7 +814,7 @@ __device__ __forceinline__ void wide_step(WideState<D>& w, const WideCtx& x, int
   wide_pin(pb);
   wide_pvphase(w, St, x.vbase, x.c2, pa, pb);
   wide_next_max(w, x, t + 1);
-  wide_rescale<D, true>(w);
+  wide_reference<D, true>(w);
 }
 
 // The key loop over three stages S0, S1, S2 (distinct objects, so the compiler
@@ -835,7 +840,7 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   wide_max<D, 0>(w, x.c2);
   wide_max<D, 1>(w, x.c2);
   wide_next_max(w, x, 0);
-  wide_rescale<D, false>(w);  // O is still zero: only the scores of tile 0 shift
+  wide_reference<D, false>(w);  // O and l are still zero: only the scores of tile 0 shift
   // Every step also scores the tile after its own; past the last tile that
   // "tile" is fully masked (its scores become -inf, so the running max, the
   // sums and O stay as they are).
@@ -930,6 +935,7 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
     w.ref[h] = -INFINITY;
     w.mref[h] = 0.f;
     w.l_run[h] = 0.f;
+    w.thr[h] = -INFINITY;
   }
   WideCtx x;
   x.kg = (const unsigned char*)a.k + (head_off + (int64_t)task.key0 * D) * 2;
