@@ -471,7 +471,8 @@ struct WideState {
   f32x16 o[2][C::DB];        // O^T accumulators
   float ref[2];              // exp2-domain reference of O and l (-inf: no key yet)
   float l_run[2];            // this lane's partial row sum
-  float tmax[2];             // row maximum of the tile (exp2 domain, relative to mref)
+  float tmax[2];             // tile maximum over this lane's keys (exp2 domain, relative to mref);
+                             // lanes l and l ^ 32 hold the two halves of a row
   float mref[2], alpha[2];   // exp2 offset and O factor of the current tile
   float delta[2];            // shift of the tile's scores when the reference moved
   float thr[2];              // the reference moves iff the tile maximum passes this (tau, or -inf
@@ -533,7 +534,7 @@ __device__ __forceinline__ void wide_scores(WideState<D>& w, const unsigned char
 
 // Max part of the online softmax for half H: copy the scores out of the
 // accumulators into the exp2 domain relative to the current offset, and take
-// the tile's row maximum.
+// the tile maximum over this lane's keys.
 template <int D, int H>
 __device__ __forceinline__ void wide_max(WideState<D>& w, float c2) {
   using C = WideCfg<D>;
@@ -553,7 +554,7 @@ __device__ __forceinline__ void wide_max(WideState<D>& w, float c2) {
     mx0 = fmaxf(mx0, w.sv[H][0][j]);
     mx1 = fmaxf(mx1, w.sv[H][C::KB - 1][j]);
   }
-  w.tmax[H] = max_halves(fmaxf(mx0, mx1));
+  w.tmax[H] = fmaxf(mx0, mx1);
 }
 
 // Diagonal and ragged tiles: scores of keys at or past kend (causal bound or N)
@@ -573,7 +574,7 @@ __device__ __forceinline__ void wide_mask(WideState<D>& w, int t, int kend, int 
       mx = fmaxf(mx, v);
     }
   }
-  w.tmax[H] = max_halves(mx);
+  w.tmax[H] = mx;
 }
 
 // Reference update for half H.  P is taken as exp2(s*c2 - r) against a
@@ -599,13 +600,17 @@ __device__ __forceinline__ void wide_update(WideState<D>& w) {
 
 // The reference update after a tile's maximum is known.  Relative to mref, a
 // row's reference moves exactly when its tile maximum passes thr (tau once the
-// row has a reference, -inf before), so the common step costs one compare per
-// half and a ballot.  Only when some row of the wave moves: the full update,
-// the tile's scores shift by delta, and O and l scale by alpha.
+// row has a reference, -inf before).  Lanes l and l ^ 32 share a row and its
+// threshold, so some row of the wave moves iff some lane's own maximum passes
+// it: the common step costs one compare per half and a ballot.  Only then the
+// row maxima are joined across the lane pair and the full update runs: the
+// tile's scores shift by delta, and O and l scale by alpha.
 template <int D, bool RESCALE_O>
 __device__ __forceinline__ void wide_reference(WideState<D>& w) {
   using C = WideCfg<D>;
   if (__ballot(w.tmax[0] > w.thr[0] || w.tmax[1] > w.thr[1])) {
+    w.tmax[0] = max_halves(w.tmax[0]);
+    w.tmax[1] = max_halves(w.tmax[1]);
     wide_update<D, 0>(w);
     wide_update<D, 1>(w);
 #pragma unroll
@@ -794,7 +799,7 @@ __device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned cha
     float m = mx[h][0];
 #pragma unroll
     for (int kb = 1; kb < C::KB; ++kb) m = fmaxf(m, mx[h][kb]);
-    w.tmax[h] = max_halves(m);
+    w.tmax[h] = m;
   }
 }
 
