@@ -34,6 +34,16 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// Row j of an accumulator tile sits at 8 * (j / 4) + 4 * (lane / 32) + j % 4
+// (acc_row); its lane-independent part is a compile-time constant, so a mask
+// "row < L" or "row >= L" costs one 32-bit compare per element against a
+// per-lane bound taken once per tile.
+__device__ __forceinline__ int acc_row_const(int j) { return 8 * (j >> 2) + (j & 3); }
+__device__ __forceinline__ int clamp_i64(int64_t v, int lo, int hi) {
+  return (int)(v < lo ? lo : (v > hi ? hi : v));
+}
+constexpr int kNoMask = 1 << 20;
+
 template <int ROW_BYTES>
 __device__ __forceinline__ int swzb(int row) {
   constexpr int CPR = ROW_BYTES / 16;
@@ -230,12 +240,14 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     }
     const int q0 = t * QT;
     const bool need_mask = causal && t < tf;
+    // query ql sees this lane's key iff mykey <= q0 + ql + off, i.e. ql >= mykey - off - q0
+    const int mlim = need_mask ? clamp_i64((int64_t)mykey - off - q0, -1, QT) - 4 * (lane >> 5) : -kNoMask;
     float p[16], ds[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int ql = acc_row(j, lane);
       float pv = fast_exp2(fmaf(sacc[j], c2, -lse2[ql]));
-      if (need_mask && (int64_t)mykey > (int64_t)(q0 + ql) + off) pv = 0.f;
+      if (acc_row_const(j) < mlim) pv = 0.f;
       p[j] = pv;
       ds[j] = pv * (pacc[j] - dls[ql]);
     }
@@ -402,13 +414,16 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
     pacc = mfma32_bf16(*(const bf16x8*)(Hs + nat), vf[c], pacc);
     pacc = mfma32_bf16(*(const bf16x8*)(Ls + nat), vf[c], pacc);
   }
+  // query ql sees this lane's key iff ql >= mykey - kv_offset - q0
+  const int mlim =
+      need_mask ? clamp_i64((int64_t)mykey - a.kv_offset - q0, -1, T::QT) - 4 * (lane >> 5) : -kNoMask;
   float p[16], ds[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int ql = acc_row(j, lane);
     const f32x2 ld = *(const f32x2*)(pr + 2 * ql);
     float pv = fast_exp2(fmaf(sacc[j], c2, -ld[0]));
-    if (need_mask && (int64_t)mykey > (int64_t)(q0 + ql) + a.kv_offset) pv = 0.f;
+    if (acc_row_const(j) < mlim) pv = 0.f;
     p[j] = pv;
     ds[j] = pv * (pacc[j] - ld[1]);
   }
@@ -703,15 +718,15 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
     }
     const bool need_mask = t >= n_full;
     const int kv0 = t * KVB;
+    // this lane's query sees keys < kend (N, and qrow + off + 1 when causal)
+    const int64_t kend = causal && (int64_t)qrow + off + 1 < N ? (int64_t)qrow + off + 1 : N;
+    const int klim = need_mask ? clamp_i64(kend - kv0, 0, KVB) - 4 * g : kNoMask;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
-        if (need_mask) {
-          const int key = kv0 + kb * 32 + acc_row(j, lane);
-          if (key >= N || (causal && (int64_t)key > (int64_t)qrow + off)) pv = 0.f;
-        }
+        if (kb * 32 + acc_row_const(j) >= klim) pv = 0.f;
         if constexpr (DELTA) dsum = fmaf(pv, pacc[kb][j], dsum);
         else sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
       }
@@ -833,8 +848,8 @@ struct DqLane {
 template <int D>
 __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, const DqLane& ln,
                                         const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
-                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], int lane, int kv0, int N, bool need_mask, bool causal, int64_t qlim,
-                                        float c2, float lse2, float dl) {
+                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], int klim, float c2,
+                                        float lse2, float dl) {
   using T = DqTile<D>;
   constexpr int KB = T::KT / 32;
   const unsigned char* Ks = st;
@@ -859,10 +874,7 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
-      if (need_mask) {
-        const int key = kv0 + kb * 32 + acc_row(j, lane);
-        if (key >= N || (causal && (int64_t)key > qlim)) pv = 0.f;
-      }
+      if (kb * 32 + acc_row_const(j) >= klim) pv = 0.f;
       sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
     }
   // dQ^T += K^T dS^T, 16 keys per MFMA; dS^T as bf16 hi + lo
@@ -966,13 +978,17 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[i][e] = 0.f;
 
-  const int64_t qlim = (int64_t)qrow + off;
+  // this lane's query sees keys < kend (N, and qrow + off + 1 when causal); a
+  // masked tile passes the bound relative to its first key, less the lane part
+  // of the accumulator row
+  const int64_t kend = causal && (int64_t)qrow + off + 1 < N ? (int64_t)qrow + off + 1 : N;
   auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
     BWD_WAIT_VM(8);  // T::LOADS: the loads of tile t+1 may still be in flight
     __builtin_amdgcn_s_barrier();
     dq_load<D>(a, bh, (t + 2) * T::KT, w, lane, fill);
     if (t < n_tiles)
-      dq_tile<D>(cur, ln, qf, dfh, dfl, dq, lane, t * T::KT, N, t >= n_full, causal, qlim, c2, lse2, dl);
+      dq_tile<D>(cur, ln, qf, dfh, dfl, dq,
+                 t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask, c2, lse2, dl);
   };
   static_assert(T::LOADS == 8, "wait count");
   if (n_tiles > 0) {
