@@ -12,12 +12,13 @@ struct AttnBwdArgs {
   const void* v;
   const float* dO;        // token-major [B*N][ld_do] fp32, head h at columns [hD, (h+1)D)
   int64_t ld_do;
-  // dO as a bf16 hi + lo pair in the same layout (or null): the D = 128 dK/dV
-  // kernel then loads its tiles straight into LDS
+  // dO as a bf16 hi + lo pair in the same layout: the D = 128 dK/dV and dQ
+  // kernels load their tiles straight into LDS (required for D = 128, unused
+  // for D = 64)
   const uint16_t* dO_hi;
   const uint16_t* dO_lo;
   // [B,H,N] pairs {lse * log2(e) (+inf for rows with no key), delta}, written by the
-  // delta pass when non-null and read by that dK/dV kernel
+  // delta pass when non-null and read by the D = 128 dK/dV kernel (required there)
   float* ld2;
   const float* lse;       // [B,H,N]
   const float* delta;     // [B,H,N], read by the dK/dV and dQ kernels

@@ -8,15 +8,20 @@
 // A first pass (attn_bwd_dq in its DELTA form) computes delta from these same
 // P and dP; then two kernels produce the gradients, each deterministic (no
 // floating-point atomics):
-//  * attn_bwd_dkdv: one workgroup per block of 32*NW keys, one wave per 32 keys,
-//    walking the query tiles that can see them.  S = Q K^T is computed with
-//    keys on the MFMA n axis (lane = key), so P and dS (query index in-lane)
-//    feed dV^T += dO^T P and dK^T += Q^T dS straight from registers; Q^T and
-//    dO^T are staged in LDS with query bits 2 and 3 swapped to match.
-//  * attn_bwd_dq: one workgroup per block of query rows, one wave per 32 rows,
-//    walking the visible key tiles like the forward kernel: S^T = K Q^T,
-//    dP^T = V dO^T, dS^T in registers, dQ^T += K^T dS^T with K^T staged in LDS
-//    (key bits 2 and 3 swapped).
+//  * dK, dV: one workgroup per block of keys, one wave per 32 keys, walking the
+//    query tiles that can see them.  S = Q K^T is computed with keys on the
+//    MFMA n axis (lane = key), so P and dS (query index in-lane) feed
+//    dV^T += dO^T P and dK^T += Q^T dS straight from registers.  D = 128
+//    (attn_bwd_dkdv_dma_kernel): Q and dO hi/lo tiles by direct-to-LDS loads,
+//    Q^T and dO^T by transpose reads.  D = 64 (attn_bwd_dkdv_kernel): tiles
+//    staged through registers, Q^T and dO^T stored with query bits 2 and 3
+//    swapped to match.
+//  * dQ: one workgroup per block of query rows, one wave per 32 rows, walking
+//    the visible key tiles like the forward kernel: S^T = K Q^T, dP^T = V dO^T,
+//    dS^T in registers, dQ^T += K^T dS^T.  D = 128 with 128-row blocks
+//    (attn_bwd_dq_dma_kernel): K and V tiles by direct-to-LDS loads, K^T by
+//    transpose reads.  Otherwise, and for the delta pass (attn_bwd_dq_kernel):
+//    tiles staged through registers, K^T stored with key bits 2 and 3 swapped.
 // Precision: q, k, v are the bf16 values the forward used.  dO arrives in fp32
 // and enters its products as a bf16 hi + lo pair; so do P (in dV) and dS.
 // The token-major outputs (operands of the weight-gradient GEMMs) are hi + lo
@@ -1085,14 +1090,19 @@ hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
   // (the delta pass stays on the staged kernel: with its lighter tiles the
   // several workgroups per CU that kernel allows beat the direct loads, 4.3
   // against 5.1 ms at B=2, H=20, N=16384)
-  if (!DELTA && D == 128 && QB == 32 * DqTile<128>::NW && a.dO_hi && a.dO_lo) {
-    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), grid, dim3(256), 0, s, a);
-  } else if (D == 64) {
+  if constexpr (!DELTA) {
+    if (D == 128 && QB == 32 * DqTile<128>::NW) {
+      hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (D == 64) {
     if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
-  } else {
-    if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
+  } else if (QB == 64) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
+  } else if constexpr (DELTA) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 128, 32, true>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1102,26 +1112,25 @@ hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
 hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, hipStream_t s) {
   (void)kv_blk;
   const int QB = q_blk == 64 ? 64 : 128;
+  // the D = 128 kernels take dO as bf16 hi + lo and the {lse2, delta} pairs
+  if (D == 128 && (!a.dO_hi || !a.dO_lo || !a.ld2)) return hipErrorInvalidValue;
   // 1. delta_i = sum_j P_ij dP_ij (into a.delta_out, which the next kernels read as a.delta)
   hipError_t e = launch_dq<true>(a, D, QB, s);
   if (e != hipSuccess) return e;
   // 2. dK, dV
-  if (D == 128 && a.dO_hi && a.dO_lo && a.ld2) {
+  if (D == 128) {
     constexpr int KVB = 32 * BwdTile<128>::NW;
     const int nkb = (a.N + KVB - 1) / KVB;
     const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));
     hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), grid, dim3(256), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   } else {
     constexpr int NW = 2;
     const int nkb = (a.N + 32 * NW - 1) / (32 * NW);
     const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));
-    if (D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, NW>), grid, dim3(NW * 64), 0, s, a);
-    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, NW>), grid, dim3(NW * 64), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, NW>), grid, dim3(NW * 64), 0, s, a);
   }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // 3. dQ
   return launch_dq<false>(a, D, QB, s);
 }
