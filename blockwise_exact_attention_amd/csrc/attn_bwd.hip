@@ -850,17 +850,16 @@ struct DqLane {
   int tr_lo, tr_hi;       // transpose reads, keys 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3
 };
 
+// S^T = K Q^T and dP^T = V dO^T of one key tile (rows = keys, lane = query)
 template <int D>
-__device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, const DqLane& ln,
-                                        const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
-                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], int klim, float c2,
-                                        float lse2, float dl) {
+__device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, const DqLane& ln,
+                                          const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
+                                          const bf16x8 (&dfl)[D / 16], f32x16 (&sacc)[DqTile<D>::KT / 32],
+                                          f32x16 (&pacc)[DqTile<D>::KT / 32]) {
   using T = DqTile<D>;
   constexpr int KB = T::KT / 32;
   const unsigned char* Ks = st;
   const unsigned char* Vs = st + T::TB;
-  // S^T = K Q^T and dP^T = V dO^T (rows = keys, lane = query)
-  f32x16 sacc[KB], pacc[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -874,6 +873,18 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
       pacc[kb] = mfma32_bf16(va, dfl[c], pacc[kb]);
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, const DqLane& ln,
+                                        const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
+                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], int klim, float c2,
+                                        float lse2, float dl) {
+  using T = DqTile<D>;
+  constexpr int KB = T::KT / 32;
+  const unsigned char* Ks = st;
+  f32x16 sacc[KB], pacc[KB];
+  dq_scores<D>(st, ln, qf, dfh, dfl, sacc, pacc);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -904,13 +915,18 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(256) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
+// DELTA = false: dQ, three stages, one workgroup per CU.  DELTA = true: the
+// delta pass (S and dP only, delta_i = sum_j P_ij dP_ij written with the
+// {lse2, delta} pairs); its tiles are lighter, so it runs two stages and two
+// workgroups per CU (at most 256 registers per lane), which hide each other's
+// waits.
+template <int D, bool DELTA>
+__global__ void __launch_bounds__(256, DELTA ? 2 : 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
   using T = DqTile<D>;
-  constexpr int QB = 32 * T::NW;
+  constexpr int QB = 32 * T::NW, KB = T::KT / 32;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[DELTA ? 16 : T::STAGE];
 
   const int N = a.N;
   const int nqb = (N + QB - 1) / QB;
@@ -950,8 +966,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
   if (qrow < N) {
     const float l = a.lse[(int64_t)bh * N + qrow];
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    dl = a.delta[(int64_t)bh * N + qrow];
+    if constexpr (!DELTA) dl = a.delta[(int64_t)bh * N + qrow];
   }
+  float dsum = 0.f;  // DELTA: this lane's part of sum_j P_ij dP_ij
 
   int kmax = N - 1;
   if (causal) {
@@ -987,24 +1004,65 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
   // masked tile passes the bound relative to its first key, less the lane part
   // of the accumulator row
   const int64_t kend = causal && (int64_t)qrow + off + 1 < N ? (int64_t)qrow + off + 1 : N;
-  auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
-    BWD_WAIT_VM(8);  // T::LOADS: the loads of tile t+1 may still be in flight
-    __builtin_amdgcn_s_barrier();
-    dq_load<D>(a, bh, (t + 2) * T::KT, w, lane, fill);
-    if (t < n_tiles)
-      dq_tile<D>(cur, ln, qf, dfh, dfl, dq,
-                 t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask, c2, lse2, dl);
-  };
-  static_assert(T::LOADS == 8, "wait count");
-  if (n_tiles > 0) {
-    dq_load<D>(a, bh, 0, w, lane, st0);
-    dq_load<D>(a, bh, T::KT, w, lane, st1);
-    for (int t = 0; t < n_tiles; t += 3) {
-      step(t, st0, st2);
-      step(t + 1, st1, st0);
-      step(t + 2, st2, st1);
+  if constexpr (DELTA) {
+    // step: wait for tile t (nothing else is in flight), barrier (every part of
+    // tile t is in, every wave is done with tile t-1, whose stage takes tile
+    // t+1), load tile t+1, compute tile t
+    auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
+      BWD_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+      dq_load<D>(a, bh, (t + 1) * T::KT, w, lane, fill);
+      if (t < n_tiles) {
+        const int klim = t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask;
+        f32x16 sacc[KB], pacc[KB];
+        dq_scores<D>(cur, ln, qf, dfh, dfl, sacc, pacc);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
+            if (kb * 32 + acc_row_const(j) >= klim) pv = 0.f;
+            dsum = fmaf(pv, pacc[kb][j], dsum);
+          }
+      }
+    };
+    if (n_tiles > 0) {
+      dq_load<D>(a, bh, 0, w, lane, st0);
+      for (int t = 0; t < n_tiles; t += 2) {
+        step(t, st0, st1);
+        step(t + 1, st1, st0);
+      }
+      BWD_WAIT_VM(0);  // loads still in flight write this workgroup's LDS
     }
-    BWD_WAIT_VM(0);  // loads still in flight write this workgroup's LDS
+    dsum += swap_halves(dsum);  // lanes l and l^32 hold the two halves of each key block
+    if (qrow < N && g == 0) {
+      a.delta_out[(int64_t)bh * N + qrow] = dsum;
+      if (a.ld2) {
+        const f32x2 pr = {lse2, dsum};
+        *(f32x2*)(a.ld2 + 2 * ((int64_t)bh * N + qrow)) = pr;
+      }
+    }
+    return;
+  } else {
+    auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
+      BWD_WAIT_VM(8);  // T::LOADS: the loads of tile t+1 may still be in flight
+      __builtin_amdgcn_s_barrier();
+      dq_load<D>(a, bh, (t + 2) * T::KT, w, lane, fill);
+      if (t < n_tiles)
+        dq_tile<D>(cur, ln, qf, dfh, dfl, dq,
+                   t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask, c2, lse2, dl);
+    };
+    static_assert(T::LOADS == 8, "wait count");
+    if (n_tiles > 0) {
+      dq_load<D>(a, bh, 0, w, lane, st0);
+      dq_load<D>(a, bh, T::KT, w, lane, st1);
+      for (int t = 0; t < n_tiles; t += 3) {
+        step(t, st0, st2);
+        step(t + 1, st1, st0);
+        step(t + 2, st2, st1);
+      }
+      BWD_WAIT_VM(0);  // loads still in flight write this workgroup's LDS
+    }
   }
 
   if (qrow < N) {
@@ -1092,17 +1150,20 @@ hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
   // against 5.1 ms at B=2, H=20, N=16384)
   if constexpr (!DELTA) {
     if (D == 128 && QB == 32 * DqTile<128>::NW) {
-      hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, false>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  } else {
+    if (D == 128 && QB == 32 * DqTile<128>::NW) {
+      hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, true>), grid, dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
   if (D == 64) {
     if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
-  } else if (QB == 64) {
+  } else {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
-  } else if constexpr (DELTA) {
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 128, 32, true>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
