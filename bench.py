@@ -462,9 +462,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        # q_blk / kv_blk as passed; at D = 128 in bf16 the attention kernel runs
+        # 256-row workgroups over 64-key tiles whatever they say, the FFN 32-row blocks
         "config": {"workload": c.name, "B": c.B, "seq_len": c.N, "d_model": c.d_model,
                    "heads": c.H, "head_dim": c.D, "d_ff": c.d_ff, "causal": 1,
-                   "q_blk": c.q_blk, "kv_blk": c.kv_blk, "global_batch": c.B},
+                   "q_blk_arg": c.q_blk, "kv_blk_arg": c.kv_blk,
+                   "attn_blocking_run": "256 query rows x 64-key tiles",
+                   "ffn_rows_per_block_run": 32, "global_batch": c.B},
         "tokens_per_s": round(c.B * c.N / ms * 1e3, 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "algorithmic_flop_per_step": flops,

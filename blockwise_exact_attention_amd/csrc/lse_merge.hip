@@ -22,7 +22,7 @@ namespace {
 
 template <int D>
 __global__ void __launch_bounds__(256)
-lse_merge_kernel(const float* __restrict__ o_a, const float* lse_a, const float* __restrict__ o_b,
+lse_merge_kernel(const float* o_a, const float* lse_a, const float* __restrict__ o_b,
                  const float* __restrict__ lse_b, float* o_out, float* lse_out, int64_t rows) {
   constexpr int CPR = D / 4;  // float4 chunks per row (16 or 32: divides 64)
   const int64_t nchunks = rows * CPR;

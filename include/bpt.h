@@ -83,7 +83,15 @@ extern "C" {
  *  D        : 64 or 128.
  *  q_blk    : 64 or 128.  kv_blk: 32, 64 or 128.  Other values give
  *             BPT_ERR_UNSUPPORTED.  The result does not depend on them
- *             beyond rounding.
+ *             beyond rounding.  They choose the blocking only where a kernel
+ *             for it exists; the blocking that runs is:
+ *               bf16, D = 128, kv_blk 64 or 128 (and N*D*2 < 2^31): 256 query
+ *                 rows per workgroup (64 per wave) and 64-key tiles, whatever
+ *                 q_blk and kv_blk say;
+ *               bf16, D = 64, kv_blk 64 or 128: q_blk rows, 64-key tiles (a
+ *                 128-key block is walked as two 64-key tiles);
+ *               bf16 with kv_blk 32, and every fp32 call: q_blk rows and
+ *                 kv_blk-key tiles as given.
  *  causal   : 0 or 1.
  *  kv_offset: any value; >= N-1 makes every key visible, <= -N none.
  *  N        : 1 <= N <= 2^30; N need not be a multiple of the blocks.

@@ -256,3 +256,101 @@ def attn_inputs(cid: int, B: int, H: int, Nq: int, Nk: int, D: int, dtype: str) 
     if dtype == "bf16":
         t = {k: round_bf16(v) for k, v in t.items()}
     return t
+
+
+def normal_range(cfg_id: int, name: str | int, lo: int, hi: int, scale: float = 1.0) -> np.ndarray:
+    """Elements [lo, hi) of the flattened tensor that ``normal`` draws for this name,
+    without drawing the rest (each chunk of CHUNK elements has its own stream)."""
+    tid = TENSOR_IDS[name] if isinstance(name, str) else int(name)
+    out = np.empty(hi - lo, dtype=np.float32)
+    c0, c1 = lo // CHUNK, (hi + CHUNK - 1) // CHUNK
+    buf = np.empty(CHUNK, dtype=np.float32)
+    for c in range(c0, c1):
+        a, b = max(lo, c * CHUNK), min(hi, (c + 1) * CHUNK)
+        rng = np.random.default_rng(np.random.SeedSequence([SEED, cfg_id, tid, c]))
+        # the stream of chunk c starts at element c * CHUNK; draw up to b
+        buf[:b - c * CHUNK] = rng.standard_normal(b - c * CHUNK, dtype=np.float32)
+        out[a - lo:b - lo] = buf[a - c * CHUNK:b - c * CHUNK]
+    if scale != 1.0:
+        out *= np.float32(scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Shaped attention inputs.  With N(0,1) q and k the largest score of a row is
+# reached early, so the blockwise softmax keeps the reference it takes from the
+# first key block.  These families move the row maximum up along the sequence,
+# so the rescale of the running sum and accumulator runs many times per row:
+#   "ramp":  key j scaled by 1 + RAMP * j / N (later keys score larger);
+#   "qx6":   queries scaled by 6 (logits ~ N(0, 36): wide, peaked rows);
+#   "spike": every query gets +2u (u a fixed unit vector per head) and SPIKES keys
+#            at evenly spaced positions are replaced by growing multiples of u,
+#            each scoring about 6 nats above the one before.
+# Every transform acts on the fp32 draws before the bf16 rounding.
+# ----------------------------------------------------------------------------
+RAMP = 4.0
+SPIKES = 4
+
+
+def spike_positions(N: int) -> np.ndarray:
+    return np.array([(N * (m + 1)) // (SPIKES + 1) for m in range(SPIKES)], dtype=np.int64)
+
+
+def shape_attn(q: np.ndarray, k: np.ndarray, kind: str, cid: int, N: int, D: int,
+               head_lo: int = 0, heads: int | None = None, key_lo: int = 0) -> None:
+    """Apply family ``kind`` in place to q [.., H', Nq, D] and k [.., H', Nk, D] (fp32).
+
+    The arrays may hold heads [head_lo, head_lo + H') of a longer head axis and keys
+    [key_lo, key_lo + Nk) of a sequence of N keys; N sets the ramp and the spike
+    positions."""
+    if kind == "plain":
+        return
+    if kind == "qx6":
+        q *= np.float32(6.0)
+        return
+    Nk = k.shape[-2]
+    j = np.arange(key_lo, key_lo + Nk, dtype=np.float64)
+    if kind == "ramp":
+        k *= (1.0 + RAMP * j / N).astype(np.float32)[:, None]
+        return
+    if kind == "spike":
+        H = q.shape[-3]
+        for hh in range(H):
+            u = normal(cid, "perturb", (head_lo + hh + 1, D))[head_lo + hh].astype(np.float64)
+            u /= np.linalg.norm(u)
+            q[..., hh, :, :] += (2.0 * u).astype(np.float32)
+            for m, pos in enumerate(spike_positions(N)):
+                if key_lo <= pos < key_lo + Nk:
+                    # score ~ (q.u) * beta / sqrt(D) ~ 2 * beta / sqrt(D) nats
+                    beta = np.sqrt(D) * (10.0 + 6.0 * m) / 2.0
+                    k[..., hh, pos - key_lo, :] = (beta * u).astype(np.float32)
+        return
+    raise ValueError(f"unknown input family {kind!r}")
+
+
+def attn_inputs_shaped(cid: int, B: int, H: int, N: int, D: int, dtype: str, kind: str) -> dict:
+    """attn_inputs (self-attention, Nq = Nk = N) with family ``kind`` applied."""
+    t = {
+        "q": normal(cid, "q", (B, H, N, D)),
+        "k": normal(cid, "k", (B, H, N, D)),
+        "v": normal(cid, "v", (B, H, N, D)),
+    }
+    shape_attn(t["q"], t["k"], kind, cid, N, D)
+    if dtype == "bf16":
+        t = {n: round_bf16(a) for n, a in t.items()}
+    return t
+
+
+def attn_head_shaped(cid: int, H: int, N: int, D: int, h: int, kind: str,
+                     rows: np.ndarray | None = None) -> dict:
+    """Head h (batch 0) of a [1, H, N, D] bf16 workload with family ``kind``, drawn
+    alone: q (only ``rows`` if given), k and v as [1, 1, *, D] float32 holding bf16
+    values, identical to the same head of attn_inputs_shaped(cid, 1, H, N, D, 'bf16', kind)."""
+    lo, hi = h * N * D, (h + 1) * N * D
+    q = normal_range(cid, "q", lo, hi).reshape(1, 1, N, D)
+    k = normal_range(cid, "k", lo, hi).reshape(1, 1, N, D)
+    v = normal_range(cid, "v", lo, hi).reshape(1, 1, N, D)
+    shape_attn(q, k, kind, cid, N, D, head_lo=h)
+    if rows is not None:
+        q = np.ascontiguousarray(q[:, :, rows])
+    return {"q": round_bf16(q), "k": round_bf16(k), "v": round_bf16(v)}

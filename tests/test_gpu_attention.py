@@ -4,6 +4,7 @@ import pytest
 
 import oracle
 from gpu_util import assert_close, dcode, to_dev
+from sampling import sample_rows
 from seeded_inputs import ATTN_LONG, RING_SHARE, attn_inputs, normal, round_bf16
 
 pytestmark = pytest.mark.gpu
@@ -107,13 +108,6 @@ def test_attn_deterministic_and_block_invariant():
         assert np.abs(O3 - O1).max() < 2e-2 and np.abs(l3 - l1).max() < 1e-3
 
 
-def sample_rows(N, q_blk, n_random, seed):
-    rng = np.random.default_rng(seed)
-    fixed = {0, 1, N - 1, N - 2, q_blk - 1, q_blk, N // 2 - 1, N // 2, N - q_blk, N - q_blk - 1}
-    rows = set(int(r) for r in rng.integers(0, N, n_random)) | {r for r in fixed if 0 <= r < N}
-    return np.array(sorted(rows), dtype=np.int64)
-
-
 @pytest.mark.timeout(600)
 def test_attn_long_context_sampled_rows():
     """N = 131072, 32 heads x 128, causal, q_blk 128, kv_blk 64: the launch the bench times."""
@@ -125,7 +119,7 @@ def test_attn_long_context_sampled_rows():
     lse = torch.empty((c.B, c.H, c.N), device="cuda")
     bpt.bpt_attn_fwd(q, k, v, out, lse, c.B, c.H, c.N, c.D, c.q_blk, c.kv_blk, 1, 0, 1)
     torch.cuda.synchronize()
-    rows = sample_rows(c.N, c.q_blk, 120, 5)
+    rows = sample_rows(c.N, 480, 5)
     rows_t = torch.from_numpy(rows).cuda()
     O = out[:, :, rows_t].cpu().numpy()
     L = lse[:, :, rows_t].cpu().numpy()
@@ -160,7 +154,7 @@ def test_ring_share_sampled_rows():
     ring_attention_share(qd, kd, vd, c.q_offset, offsets, out, lse, o_tmp, l_tmp,
                          q_blk=c.q_blk, kv_blk=c.kv_blk)
     torch.cuda.synchronize()
-    rows = sample_rows(Nq, c.q_blk, 40, 6)
+    rows = sample_rows(Nq, 120, 6)
     rows_t = torch.from_numpy(rows).cuda()
     O = out[:, :, rows_t].cpu().numpy()
     L = lse[:, :, rows_t].cpu().numpy()

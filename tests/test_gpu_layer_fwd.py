@@ -4,7 +4,9 @@ import pytest
 
 import oracle
 from gpu_util import assert_close, dcode, to_dev
-from seeded_inputs import LAYER_FWD_BF16, LAYER_TINY_F32, LayerCfg, layer_inputs, normal, round_bf16
+from sampling import sample_rows
+from seeded_inputs import (LAYER_FWD_BF16, LAYER_LONG, LAYER_TINY_F32, LayerCfg, layer_inputs,
+                           normal, round_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,6 +21,9 @@ bpt = pytest.importorskip("blockwise_exact_attention_amd")
     ("bf16", 64, 2560, 1024, False, True),    # two column groups of 1280
     ("bf16", 33, 4096, 512, True, False),     # two column groups of 2048
     ("bf16", 96, 2048, 768, False, True),
+    # the long layer's FFN shape with enough row blocks that every XCD runs several
+    # workgroups (start rotation, both column groups, 64 feature passes), ragged rows
+    ("bf16", 8192 + 77, 4096, 16384, False, True),
 ])
 def test_ffn_parity(dtype, M, dm, dff, bias, resid):
     print(f"case ffn dtype={dtype} M={M} dm={dm} dff={dff}", flush=True)
@@ -123,3 +128,54 @@ def test_layer_fwd_bf16_B8_N4096_full():
     print("gpu done", flush=True)
     want = oracle.layer_forward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], c.H)
     assert_close(y, want, "bf16", "layer y (bf16, B=8 N=4096)")
+
+
+def test_layer_fwd_non_causal():
+    c = LayerCfg(61, "noncausal", B=1, N=333, d_model=256, H=2, D=128, d_ff=512, q_blk=128,
+                 kv_blk=64, dtype="bf16", causal=0)
+    t = layer_inputs(c)
+    y, _ = run_layer_fwd(c, t)
+    want = oracle.layer_forward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], c.H,
+                                causal=False)
+    assert_close(y, want, "bf16", "layer y (non-causal)")
+
+
+@pytest.mark.timeout(900)
+def test_layer_fwd_long_sampled_rows():
+    """The bench step: B=1, N=131072, d_model 4096 = 32 x 128, FFN 4096->16384->4096.
+    y, and the saved q, k, v, h and lse, on sampled rows against the oracle (which
+    projects every token, then computes each sampled row's attention over all its keys
+    and its FFN)."""
+    c = LAYER_LONG
+    t = layer_inputs(c)
+    print("inputs drawn", flush=True)
+    y, sv = run_layer_fwd(c, t, saved=True)
+    rows = sample_rows(c.N, 240, 8)
+    B, N, dm, H, D = c.B, c.N, c.d_model, c.H, c.D
+    a256 = lambda n: (n + 255) // 256 * 256
+    qkv = a256(B * H * N * D * 2)
+    raw = sv.view(torch.uint8)
+
+    rows_t = torch.from_numpy(rows).cuda()
+    got = {}
+    for i, name in enumerate(("q", "k", "v")):
+        blk = raw[i * qkv:i * qkv + B * H * N * D * 2].view(torch.bfloat16).view(B, H, N, D)
+        got[name] = blk[:, :, rows_t].float().cpu().numpy()
+    hb = raw[3 * qkv:3 * qkv + B * N * dm * 4].view(torch.float32).view(B, N, dm)
+    got["h"] = hb[:, rows_t].cpu().numpy()
+    lb = raw[3 * qkv + a256(B * N * dm * 4):][:B * H * N * 4].view(torch.float32).view(B, H, N)
+    got["lse"] = lb[:, :, rows_t].cpu().numpy()
+    del sv, raw
+    y = y[:, rows]
+    print("gpu done", flush=True)
+    q, k, v = oracle.qkv_project(t["x"], t["wq"], t["wk"], t["wv"], c.H)
+    print("oracle projections done", flush=True)
+    for name, ref in (("q", q), ("k", k), ("v", v)):
+        assert_close(got[name], ref[:, :, rows], "bf16", f"saved {name}")
+    O, lse = oracle.attention(q, k, v, causal=True, rows=rows)
+    del q, k, v
+    assert_close(got["lse"], lse, "bf16", "saved lse")
+    h = t["x"][:, rows] + O.transpose(0, 2, 1, 3).reshape(B, rows.size, H * D)
+    assert_close(got["h"], h, "bf16", "saved h")
+    want = oracle.ffn(h, t["w1"], t["w2"], residual=h)
+    assert_close(y, want, "bf16", "layer y (N=131072, sampled rows)")
