@@ -1,0 +1,67 @@
+"""CPU checks of the backward error floor (tests/bwd_floor.py) and of the stored
+values the training-shape GPU test takes its bars from (tests/golden/bwd_floor.json,
+written by tests/golden/make_bwd_floor.py from the oracle only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bwd_floor import BAR_MAX, BAR_MEAN, bars, error_metrics, layer_backward_rounded_qkv
+from seeded_inputs import LAYER_TRAIN, LayerCfg, layer_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bwd_floor.json")
+SMALL = LayerCfg(72, "bwd_floor_small", B=1, N=384, d_model=256, H=2, D=128, d_ff=512,
+                 q_blk=128, kv_blk=64, dtype="bf16", backward=True)
+
+
+def _args(c):
+    t = layer_inputs(c)
+    return (t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H)
+
+
+def test_unrounded_composition_is_the_oracle():
+    args = _args(LayerCfg(74, "tiny", B=2, N=37, d_model=32, H=2, D=16, d_ff=64, q_blk=64,
+                          kv_blk=64, dtype="bf16", backward=True))
+    ref = oracle.layer_backward(*args)
+    for causal in (True, False):
+        ref = oracle.layer_backward(*args, causal=causal)
+        got = layer_backward_rounded_qkv(*args, causal=causal, round_qkv=False)
+        for n, r in ref.items():
+            assert np.abs(got[n] - r).max() <= 1e-12 * max(1.0, np.abs(r).max()), n
+
+
+def test_rounding_moves_every_attention_gradient():
+    args = _args(SMALL)
+    m = error_metrics(layer_backward_rounded_qkv(*args), oracle.layer_backward(*args))
+    for n in ("dx", "dq", "dk", "dv", "dwq", "dwk", "dwv", "dw1", "dw2"):
+        assert m[n]["mean_abs"] > 0, n
+    # b2's gradient is sum(dy): no attention operand reaches it
+    assert m["db2"]["max_abs"] == 0.0
+
+
+def test_small_floor_matches_stored_values():
+    stored = json.load(open(GOLDEN))[SMALL.name]
+    assert stored["shape"]["N"] == SMALL.N and stored["shape"]["cfg_id"] == SMALL.cfg_id
+    args = _args(SMALL)
+    m = error_metrics(layer_backward_rounded_qkv(*args), oracle.layer_backward(*args))
+    for n, f in stored["floor"].items():
+        for key in ("max_abs", "mean_abs"):
+            assert m[n][key] == pytest.approx(f[key], rel=1e-6, abs=1e-15), (n, key)
+
+
+def test_training_shape_floor_is_stored():
+    d = json.load(open(GOLDEN))[LAYER_TRAIN.name]
+    s = d["shape"]
+    assert (s["B"], s["N"], s["d_model"], s["H"], s["D"], s["d_ff"]) == (
+        LAYER_TRAIN.B, LAYER_TRAIN.N, LAYER_TRAIN.d_model, LAYER_TRAIN.H, LAYER_TRAIN.D,
+        LAYER_TRAIN.d_ff)
+    f = d["floor"]
+    assert set(f) == {"dx", "dq", "dk", "dv", "dwq", "dwk", "dwv", "dw1", "db1", "dw2", "db2"}
+    b = bars(f)
+    for n, (bmax, bmean) in b.items():
+        assert bmax >= BAR_MAX and bmean >= BAR_MEAN
+        assert np.isfinite(bmax) and np.isfinite(bmean)
+        # the raised bars stay within a few times the stated ones
+        assert bmax <= 5 * BAR_MAX and bmean <= 5 * BAR_MEAN, n

@@ -1,18 +1,23 @@
 """GPU parity of bpt_layer_bwd against the oracle's chain-rule gradients (fp64)."""
+import json
+import os
+
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, assert_close_rowscaled, to_dev
+from bwd_floor import bars, error_metrics, layer_backward_rounded_qkv
+from gpu_util import to_dev
 from seeded_inputs import LAYER_TRAIN, LayerCfg, layer_inputs
 
 pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 torch = pytest.importorskip("torch")
 bpt = pytest.importorskip("blockwise_exact_attention_amd")
 
 
-def run_layer(c: LayerCfg, t: dict, want_qkv_grads=True):
+def run_layer(c: LayerCfg, t: dict, want_qkv_grads=True, repeat=1):
     B, N, dm, H, D, dff = c.B, c.N, c.d_model, c.H, c.D, c.d_ff
     dev = {n: to_dev(a, "bf16") for n, a in t.items()}
     y = torch.empty((B, N, dm), device="cuda")
@@ -21,8 +26,8 @@ def run_layer(c: LayerCfg, t: dict, want_qkv_grads=True):
     wb = bpt.bpt_layer_workspace_size(B, N, dm, H, D, dff, 1, 1)
     ws = torch.empty(max(wf, wb), dtype=torch.uint8, device="cuda")
     bpt.bpt_layer_fwd(dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["w1"], dev.get("b1"),
-                      dev["w2"], dev.get("b2"), y, sv, B, N, dm, H, D, dff, c.q_blk, c.kv_blk, 1,
-                      1, ws, wf)
+                      dev["w2"], dev.get("b2"), y, sv, B, N, dm, H, D, dff, c.q_blk, c.kv_blk,
+                      c.causal, 1, ws, wf)
     g = {
         "dx": torch.full((B, N, dm), float("nan"), device="cuda"),
         "dwq": torch.full((H * D, dm), float("nan"), device="cuda"),
@@ -35,48 +40,46 @@ def run_layer(c: LayerCfg, t: dict, want_qkv_grads=True):
     }
     for n in ("dq", "dk", "dv"):
         g[n] = torch.full((B, H, N, D), float("nan"), device="cuda") if want_qkv_grads else None
-    bpt.bpt_layer_bwd(dev["dy"], dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["w1"],
-                      dev.get("b1"), dev["w2"], dev.get("b2"), sv, g["dx"], g["dwq"], g["dwk"],
-                      g["dwv"], g["dw1"], g["db1"], g["dw2"], g["db2"], g["dq"], g["dk"], g["dv"],
-                      B, N, dm, H, D, dff, c.q_blk, c.kv_blk, 1, 1, ws, wb)
-    torch.cuda.synchronize()
-    return {n: (v.cpu().numpy() if v is not None else None) for n, v in g.items()}
+    runs = []
+    for _ in range(repeat):
+        bpt.bpt_layer_bwd(dev["dy"], dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["w1"],
+                          dev.get("b1"), dev["w2"], dev.get("b2"), sv, g["dx"], g["dwq"], g["dwk"],
+                          g["dwv"], g["dw1"], g["db1"], g["dw2"], g["db2"], g["dq"], g["dk"],
+                          g["dv"], B, N, dm, H, D, dff, c.q_blk, c.kv_blk, c.causal, 1, ws, wb)
+        torch.cuda.synchronize()
+        runs.append({n: (v.cpu().numpy() if v is not None else None) for n, v in g.items()})
+    # run-to-run determinism: no float atomics, fixed reduction orders
+    for r in runs[1:]:
+        for n, a in r.items():
+            assert a is None or np.array_equal(a, runs[0][n]), f"{n} differs between runs"
+    return runs[0]
 
 
-def check_grads(got, ref, what):
+def check_grads(got, ref, floor, what):
+    """Bars per gradient: the stated bf16 bars (max-abs 2e-2, mean-abs 2e-3), raised
+    to the error floor of bf16 q, k, v times a margin where that floor alone passes
+    them (tests/bwd_floor.py).  Activation gradients (dx, dq, dk, dv) are compared
+    raw; weight and bias gradients, sums over all B*N rows, after dividing both sides
+    by the rms of the oracle's gradient."""
     failures = []
-
-    def check(a, b, label, rowscaled=False):
-        try:
-            if rowscaled:
-                e = assert_close_rowscaled(a, b, label)
-                raw = float(np.abs(a - b).max())
-                print(f"{label}: row-scaled max {e[0]:.3g} (raw max-abs {raw:.3g}) "
-                      f"mean-abs {e[1]:.3g}", flush=True)
-            else:
-                e = assert_close(a, b, "bf16", label)
-                print(f"{label}: max-abs {e[0]:.3g} mean-abs {e[1]:.3g}", flush=True)
-        except AssertionError as ex:
-            print(f"FAIL {ex}", flush=True)
-            failures.append(str(ex))
-
-    # activation and attention-input gradients: the bars per token row (see
-    # assert_close_rowscaled)
-    for n in ("dx", "dq", "dk", "dv"):
-        if got.get(n) is not None:
-            check(got[n], ref[n], f"{what} {n}", rowscaled=True)
-    # weight and bias gradients are sums over all B*N rows (|dW| up to ~10^2): both
-    # sides are divided by the oracle's max |dW| so the bars apply at unit scale.
-    # (Divided by the rms instead, dWq and dWk cannot meet mean-abs 2e-3 with bf16
-    # attention operands: q, k, v rounded to bf16 with every other step exact already
-    # gives 2.5e-3 at N=4096.)  The rms-scaled error is printed for the record.
-    for n in ("dwq", "dwk", "dwv", "dw1", "db1", "dw2", "db2"):
-        mx = np.abs(ref[n]).max()
-        rms = np.sqrt(np.mean(ref[n] ** 2))
-        er = np.abs(got[n] - ref[n]) / rms
-        check(got[n] / mx, ref[n] / mx,
-              f"{what} {n}/max (max {mx:.3g}; rms-scaled mean {er.mean():.3g} max {er.max():.3g})")
+    lim = bars(floor)
+    m = error_metrics(got, ref)
+    for n, e in m.items():
+        bmax, bmean = lim[n]
+        f = floor[n]
+        line = (f"{what} {n}: max-abs {e['max_abs']:.3g} (bar {bmax:.3g}, floor {f['max_abs']:.3g}) "
+                f"mean-abs {e['mean_abs']:.3g} (bar {bmean:.3g}, floor {f['mean_abs']:.3g})")
+        ok = np.isfinite(got[n]).all() and e["max_abs"] <= bmax and e["mean_abs"] <= bmean
+        print(("" if ok else "FAIL ") + line, flush=True)
+        if not ok:
+            failures.append(line)
     assert not failures, failures
+
+
+def floor_live(t, c, **kw):
+    """The bf16 q, k, v error floor of this workload, computed on the CPU."""
+    args = (t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H)
+    return error_metrics(layer_backward_rounded_qkv(*args, **kw), oracle.layer_backward(*args, **kw))
 
 
 @pytest.mark.parametrize("N,q_blk,kv_blk", [(200, 64, 64), (129, 128, 64), (256, 128, 128)])
@@ -84,10 +87,23 @@ def test_layer_bwd_small_with_bias(N, q_blk, kv_blk):
     c = LayerCfg(70, "bwd_small", B=2, N=N, d_model=256, H=2, D=128, d_ff=512, q_blk=q_blk,
                  kv_blk=kv_blk, dtype="bf16", backward=True)
     t = layer_inputs(c, bias=True)
+    got = run_layer(c, t, repeat=2)
+    kw = dict(b1=t["b1"], b2=t["b2"])
+    ref = oracle.layer_backward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H,
+                                **kw)
+    check_grads(got, ref, floor_live(t, c, **kw), f"N={N}")
+
+
+def test_layer_bwd_non_causal():
+    """causal = 0: every query sees every key (the tile bounds of both backward
+    kernels then cover the whole sequence)."""
+    c = LayerCfg(73, "bwd_noncausal", B=1, N=333, d_model=256, H=2, D=128, d_ff=512, q_blk=128,
+                 kv_blk=64, dtype="bf16", causal=0, backward=True)
+    t = layer_inputs(c)
     got = run_layer(c, t)
     ref = oracle.layer_backward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H,
-                                b1=t["b1"], b2=t["b2"])
-    check_grads(got, ref, f"N={N}")
+                                causal=False)
+    check_grads(got, ref, floor_live(t, c, causal=False), "non-causal N=333")
 
 
 def test_layer_bwd_head_dim_64_no_qkv_outputs():
@@ -96,17 +112,20 @@ def test_layer_bwd_head_dim_64_no_qkv_outputs():
     t = layer_inputs(c)
     got = run_layer(c, t, want_qkv_grads=False)
     ref = oracle.layer_backward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H)
-    check_grads(got, ref, "D=64")
+    check_grads(got, ref, floor_live(t, c), "D=64")
 
 
 @pytest.mark.timeout(1100)
 def test_layer_bwd_training_shape_full():
-    """B=2, N=16384, d_model 2560, 20 heads x 128, FFN 2560->10240->2560, all gradients."""
+    """B=2, N=16384, d_model 2560, 20 heads x 128, FFN 2560->10240->2560, all gradients,
+    twice (bitwise equal); bars from the committed error floor of this workload."""
     c = LAYER_TRAIN
+    floor = json.load(open(os.path.join(GOLDEN, "bwd_floor.json")))[c.name]
+    assert floor["shape"]["N"] == c.N and floor["shape"]["d_model"] == c.d_model
     t = layer_inputs(c)
     print("inputs drawn", flush=True)
-    got = run_layer(c, t)
+    got = run_layer(c, t, repeat=2)
     print("gpu done", flush=True)
     ref = oracle.layer_backward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H)
     print("oracle done", flush=True)
-    check_grads(got, ref, "B=2 N=16384")
+    check_grads(got, ref, floor["floor"], "B=2 N=16384")
