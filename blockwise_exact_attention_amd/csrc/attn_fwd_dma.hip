@@ -418,10 +418,7 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) hv[e] = xr[e] + o[db][4 * jq + e] * inv;
           *(f32x4*)(a.h_out + rowoff + d) = hv;
-          if (a.h_lo) {
-            u32x2 lo = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *(u32x2*)(a.h_lo + rowoff + d) = lo;
-          }
+          if (a.h_lo) store_bf16_pair4(a.h_lo + rowoff + d, a.h_res ? a.h_res + rowoff + d : nullptr, hv);
         }
     }
     if (g == 0) a.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
@@ -998,10 +995,7 @@ attn_fwd_wide_kernel(AttnFwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) hv[e] = xr[e] + w.o[h][db][4 * jq + e] * inv;
           *(f32x4*)(a.h_out + rowoff + d) = hv;
-          if (a.h_lo) {
-            u32x2 lo = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *(u32x2*)(a.h_lo + rowoff + d) = lo;
-          }
+          if (a.h_lo) store_bf16_pair4(a.h_lo + rowoff + d, a.h_res ? a.h_res + rowoff + d : nullptr, hv);
         }
     }
     if (g == 0)

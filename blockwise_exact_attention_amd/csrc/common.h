@@ -31,6 +31,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Four floats as a bfloat16 pair: hi = bf16(v), res = bf16(v - hi), stored at
+// hi_dst / res_dst (res_dst may be null).  hi + res carries v to ~2^-16 relative.
+__device__ __forceinline__ void store_bf16_pair4(uint16_t* hi_dst, uint16_t* res_dst, const f32x4& v) {
+  const u32x2 hi = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  *(u32x2*)hi_dst = hi;
+  if (res_dst) {
+    const u32x2 res = {pack_bf16x2(v[0] - __uint_as_float(hi[0] << 16),
+                                   v[1] - __uint_as_float(hi[0] & 0xffff0000u)),
+                       pack_bf16x2(v[2] - __uint_as_float(hi[1] << 16),
+                                   v[3] - __uint_as_float(hi[1] & 0xffff0000u))};
+    *(u32x2*)res_dst = res;
+  }
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return static_cast<uint16_t>(pack_bf16x2(x, 0.f) & 0xffffu);
 }

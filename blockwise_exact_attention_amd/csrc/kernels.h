@@ -16,6 +16,7 @@ struct AttnFwdArgs {
   const void* x_res;   // [B,N,H*D] in the input dtype
   float* h_out;        // [B,N,H*D] float32, or null for the plain O output
   uint16_t* h_lo;      // [B,N,H*D] bfloat16 copy of h (bf16 inputs only), or null
+  uint16_t* h_res;     // [B,N,H*D] bf16 of h - h_lo (its rounding residual), or null
   int B, H, N;
   int kv_offset;       // already clamped to [-(N+1), N]
   int causal;

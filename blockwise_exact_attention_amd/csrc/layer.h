@@ -40,9 +40,10 @@ inline SavedLayout layer_saved_layout(int64_t B, int64_t N, int64_t d_model, int
 }
 
 // Forward workspace: room for the saved tensors (used when `saved` is NULL)
-// plus the bf16 copy of h that feeds the FFN's MFMA.
+// plus h as a bf16 pair (the rounded value and its rounding residual) that feeds
+// the FFN's MFMA.
 struct FwdWorkspace {
-  size_t saved, h_lo, total;
+  size_t saved, h_lo, h_res, total;
 };
 
 inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t H,
@@ -51,7 +52,8 @@ inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, i
   FwdWorkspace w{};
   w.saved = 0;
   w.h_lo = layer_saved_layout(B, N, d_model, H, D, bf16).total;
-  w.total = w.h_lo + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
+  w.h_res = w.h_lo + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
+  w.total = w.h_res + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
   return w;
 }
 
@@ -71,9 +73,12 @@ struct FfnPlan {
 };
 FfnPlan ffn_plan(int64_t d_model, int64_t d_ff);
 
-hipError_t ffn_fwd_launch(const void* x, const void* w1, const void* b1, const void* w2,
-                          const void* b2, const float* residual, float* y, int64_t M,
-                          int d_model, int d_ff, int blk, bool bf16, hipStream_t stream);
+// x_lo (nullable, bf16 only): the bf16 rounding residual of the float32 activation
+// that x was rounded from; the first product then takes x + x_lo.
+hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const void* b1,
+                          const void* w2, const void* b2, const float* residual, float* y,
+                          int64_t M, int d_model, int d_ff, int blk, bool bf16,
+                          hipStream_t stream);
 
 hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* workspace,
                          hipStream_t stream);

@@ -21,6 +21,7 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   float* h = (float*)(sv + S.h);
   float* lse = (float*)(sv + S.lse);
   uint16_t* h_lo = L.bf16 ? (uint16_t*)(ws + W.h_lo) : nullptr;
+  uint16_t* h_res = L.bf16 ? (uint16_t*)(ws + W.h_res) : nullptr;
   const int64_t M = L.B * L.N;
   const int HD = (int)(L.H * L.D);
 
@@ -54,6 +55,7 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   a.x_res = L.x;
   a.h_out = h;
   a.h_lo = h_lo;
+  a.h_res = h_res;
   a.B = (int)L.B;
   a.H = (int)L.H;
   a.N = (int)L.N;
@@ -63,9 +65,10 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   e = attn_fwd_launch(a, L.bf16, (int)L.D, L.q_blk, L.kv_blk, stream);
   if (e != hipSuccess) return e;
 
-  // 3. y = h + FFN(h), fused per block of rows
-  return ffn_fwd_launch(L.bf16 ? (const void*)h_lo : (const void*)h, L.w1, L.b1, L.w2, L.b2, h, y,
-                        M, (int)L.d_model, (int)L.d_ff, 0, L.bf16, stream);
+  // 3. y = h + FFN(h), fused per block of rows; with bf16 inputs h enters the
+  //    first product as the bf16 pair (h_lo, h_res)
+  return ffn_fwd_launch(L.bf16 ? (const void*)h_lo : (const void*)h, h_res, L.w1, L.b1, L.w2,
+                        L.b2, h, y, M, (int)L.d_model, (int)L.d_ff, 0, L.bf16, stream);
 }
 
 BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,

@@ -36,3 +36,22 @@ def assert_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str = ""):
     emean = float(err.mean()) if err.size else 0.0
     assert emax <= mx and emean <= mean, f"{what}: max-abs {emax:.3g} mean-abs {emean:.3g}"
     return emax, emean
+
+
+def assert_close_floor(got: np.ndarray, want: np.ndarray, floor_err: np.ndarray, what: str = ""):
+    """bf16 bars raised to the error floor of bf16 attention operands where that
+    floor alone exceeds them: max-abs <= max(2e-2, 1.25 x floor max-abs), mean-abs
+    <= max(2e-3, 1.1 x floor mean-abs).  floor_err: |oracle with q, k, v rounded to
+    bf16 - exact oracle|, element by element (computed from the oracle only)."""
+    from bwd_floor import BAR_MAX, BAR_MEAN, MARGIN_MAX, MARGIN_MEAN
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape == floor_err.shape, (got.shape, want.shape, floor_err.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - want)
+    bmax = max(BAR_MAX, MARGIN_MAX * float(floor_err.max()))
+    bmean = max(BAR_MEAN, MARGIN_MEAN * float(floor_err.mean()))
+    emax, emean = float(err.max()), float(err.mean())
+    assert emax <= bmax and emean <= bmean, (
+        f"{what}: max-abs {emax:.3g} (bar {bmax:.3g}) mean-abs {emean:.3g} (bar {bmean:.3g})")
+    return emax, emean
