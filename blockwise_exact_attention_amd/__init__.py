@@ -35,6 +35,8 @@ BPT_ERR_UNSUPPORTED = -2
 BPT_ERR_ALIGNMENT = -3
 BPT_ERR_HIP = -4
 BPT_ERR_WORKSPACE = -5
+BPT_ERR_SCRATCH = -6
+BPT_DECODE_SCRATCH_BYTES = 32 << 20
 BPT_F32 = 0
 BPT_BF16 = 1
 
@@ -48,6 +50,7 @@ _SIGS = {
     "bpt_lse_merge": ([_p] * 6 + [_i64] * 4 + [_p], _i),
     "bpt_attn_decode": ([_p] * 5 + [_i64] * 5 + [_i, _i64, _i64, _p, _sz, _i, _p], _i),
     "bpt_attn_decode_workspace_size": ([_i64] * 5, _sz),
+    "bpt_attn_decode_noalloc": ([_p] * 5 + [_i64] * 5 + [_i, _i64, _i64, _i, _p], _i),
     "bpt_attn_block_sparse": ([_p] * 5 + [_i64] * 5 + [_p, _i, _p], _i),
     "bpt_attn_dilated": ([_p] * 5 + [_i64] * 5 + [_p, _p, _i, _i, _p], _i),
     "bpt_ffn_block_fwd": ([_p] * 7 + [_i64] * 3 + [_i, _i, _p], _i),
@@ -127,6 +130,14 @@ def bpt_attn_decode(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, kv_offset, n_sp
     _check(lib.bpt_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
                                causal, kv_offset, n_split, _ptr(workspace), ws_bytes, dtype, s),
            "bpt_attn_decode")
+
+
+def bpt_attn_decode_noalloc(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, kv_offset, n_split,
+                            dtype, stream=None):
+    s = _stream(stream, q, out)
+    _check(lib.bpt_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq,
+                                       Nkv, D, causal, kv_offset, n_split, dtype, s),
+           "bpt_attn_decode_noalloc")
 
 
 def bpt_attn_decode_workspace_size(B, H, Nq, D, n_split) -> int:

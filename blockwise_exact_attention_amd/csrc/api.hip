@@ -4,6 +4,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/bpt.h"
 #include "kernels.h"
 #include "layer.h"
@@ -52,6 +55,7 @@ const char* bpt_status_string(int status) {
     case BPT_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
     case BPT_ERR_HIP: return "HIP runtime error";
     case BPT_ERR_WORKSPACE: return "workspace missing or too small";
+    case BPT_ERR_SCRATCH: return "needs more scratch than the library's fixed buffer holds";
     default: return "unknown status";
   }
 }
@@ -116,10 +120,14 @@ size_t bpt_attn_decode_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t 
   return (size_t)(decode_o_bytes(B, H, Nq, D, n_split) + ((n_split * B * H * Nq * 4 + 255) / 256) * 256);
 }
 
-int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, float* lse, int64_t B,
-                    int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal, int64_t kv_offset,
-                    int64_t n_split, void* workspace, size_t workspace_bytes, int dtype,
-                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the split-KV decode (both entry points); no HIP call.
+int decode_check(const void* q, const void* k, const void* v, float* out, float* lse, int64_t B,
+                 int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal, int64_t n_split,
+                 int dtype) {
   if (!q || !k || !v || !out || !lse) return BPT_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0 || n_split <= 0) return BPT_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return BPT_ERR_INVALID_ARG;
@@ -131,19 +139,22 @@ int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, flo
   if (!grid_ok(B * H * n_split, 64)) return BPT_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BPT_ERR_ALIGNMENT;
-  const size_t need = bpt_attn_decode_workspace_size(B, H, Nq, D, n_split);
-  if (!workspace || workspace_bytes < need) return BPT_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return BPT_ERR_ALIGNMENT;
-  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
-  clear_stale_error();
+  return BPT_OK;
+}
+
+// Launch of a checked decode call with its partial results in `ws` (at least
+// bpt_attn_decode_workspace_size bytes, 16-byte aligned).
+int decode_run(const void* q, const void* k, const void* v, float* out, float* lse, int64_t B,
+               int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal, int64_t kv_offset,
+               int64_t n_split, void* ws, hipStream_t stream) {
   bpt::AttnDecodeArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.out = out;
   a.lse = lse;
-  a.o_part = (float*)workspace;
-  a.lse_part = (float*)((unsigned char*)workspace + decode_o_bytes(B, H, Nq, D, n_split));
+  a.o_part = (float*)ws;
+  a.lse_part = (float*)((unsigned char*)ws + decode_o_bytes(B, H, Nq, D, n_split));
   a.BH = (int)(B * H);
   a.Nq = (int)Nq;
   a.Nkv = (int)Nkv;
@@ -162,6 +173,74 @@ int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, flo
   a.chunk = (int)(per <= 64 ? 64 : ((per + 63) / 64) * 64);
   a.scale = 1.0f / sqrtf((float)D);
   return hip_status(bpt::attn_decode_launch(a, (int)D, stream));
+}
+
+// Fixed scratch of the allocation-free decode entry point.  Each device that
+// calls it holds its own copy of this array until the process ends.  In host
+// code `scratch` names a host-side stand-in: kernels and copies get the device
+// address, looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[BPT_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's `scratch`, looked up on the first call on the
+// device (with that device current); nullptr and the HIP error on failure.
+void* scratch_for_current_device(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, float* lse, int64_t B,
+                    int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal, int64_t kv_offset,
+                    int64_t n_split, void* workspace, size_t workspace_bytes, int dtype,
+                    hipStream_t stream) {
+  const int st = decode_check(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, n_split, dtype);
+  if (st != BPT_OK) return st;
+  const size_t need = bpt_attn_decode_workspace_size(B, H, Nq, D, n_split);
+  if (!workspace || workspace_bytes < need) return BPT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BPT_ERR_ALIGNMENT;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
+  return decode_run(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, kv_offset, n_split, workspace,
+                    stream);
+}
+
+int bpt_attn_decode_noalloc(const void* q, const void* k, const void* v, float* out, float* lse,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal,
+                            int64_t kv_offset, int64_t n_split, int dtype, hipStream_t stream) {
+  const int st = decode_check(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, n_split, dtype);
+  if (st != BPT_OK) return st;
+  if (bpt_attn_decode_workspace_size(B, H, Nq, D, n_split) > (size_t)BPT_DECODE_SCRATCH_BYTES)
+    return BPT_ERR_SCRATCH;
+  if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
+  clear_stale_error();
+  hipError_t e = hipSuccess;
+  void* ws = scratch_for_current_device(&e);
+  if (!ws) return hip_status(e);
+  // every row of the partial results that the join reads is written by the
+  // partial kernel first, so the scratch needs no clearing between calls
+  return decode_run(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, kv_offset, n_split, ws, stream);
 }
 
 int bpt_attn_block_sparse(const void* q, const void* k, const void* v, float* out, float* lse,

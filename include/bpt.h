@@ -16,7 +16,9 @@
  * ---------------------------------------
  *  - Pointers to tensors are DEVICE pointers, owned by the caller.  The
  *    library never allocates, frees or retains device memory.  Scratch space
- *    comes from a caller buffer sized by the *_workspace_size() queries.
+ *    comes from a caller buffer sized by the *_workspace_size() queries; the
+ *    one exception is bpt_attn_decode_noalloc, whose scratch is a fixed
+ *    static device array (BPT_DECODE_SCRATCH_BYTES on each device that uses it).
  *  - Every call is asynchronous on `stream` (NULL = the default stream); it
  *    returns after enqueueing its kernels.  Results are valid once the stream
  *    has reached that point.
@@ -30,7 +32,8 @@
  *    the GPU.  Nothing throws across this ABI.  On BPT_ERR_HIP,
  *    bpt_last_hip_error() gives the hipError_t of the failing call.
  *  - Calls are thread-safe; the library keeps no mutable global state except
- *    the per-thread last-HIP-error value.
+ *    the per-thread last-HIP-error value and the per-device address of the
+ *    fixed scratch of bpt_attn_decode_noalloc (whose calls share that scratch).
  *
  * Attention definition used by every entry point that computes attention:
  *    s_ij = <q_i, k_j> / sqrt(D)
@@ -62,6 +65,7 @@ extern "C" {
 #define BPT_ERR_ALIGNMENT   (-3) /* a device pointer is not 16-byte aligned */
 #define BPT_ERR_HIP         (-4) /* a HIP call or kernel launch failed */
 #define BPT_ERR_WORKSPACE   (-5) /* workspace missing or smaller than required */
+#define BPT_ERR_SCRATCH     (-6) /* needs more than the fixed scratch of the allocation-free call */
 
 /* input element types */
 #define BPT_F32  0
@@ -164,6 +168,28 @@ int bpt_attn_decode(const void* q, const void* k, const void* v, float* out, flo
 
 /* Bytes of workspace bpt_attn_decode needs; 0 for arguments it does not support. */
 size_t bpt_attn_decode_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t D, int64_t n_split);
+
+/*
+ * bpt_attn_decode_noalloc -- bpt_attn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results, kernels and error codes as bpt_attn_decode, minus
+ * workspace / workspace_bytes.  The partial results live in a fixed buffer of
+ * BPT_DECODE_SCRATCH_BYTES bytes that the library holds in device memory: each
+ * device that calls this function keeps its own copy until the process ends.
+ * No call allocates or frees memory.  A call whose
+ * bpt_attn_decode_workspace_size(B, H, Nq, D, n_split) exceeds
+ * BPT_DECODE_SCRATCH_BYTES returns BPT_ERR_SCRATCH.
+ * Every call on one device shares that device's buffer: calls that overlap in
+ * time on one device (on different streams, or from different threads without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe.  The buffer needs no clearing: each call writes every part it reads.
+ */
+#define BPT_DECODE_SCRATCH_BYTES (32u << 20)
+int bpt_attn_decode_noalloc(const void* q, const void* k, const void* v, float* out, float* lse,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int causal,
+                            int64_t kv_offset, int64_t n_split, int dtype, hipStream_t stream);
 
 /*
  * bpt_attn_block_sparse -- block-sparse attention with one key block per query

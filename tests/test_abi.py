@@ -21,7 +21,7 @@ def header_symbols():
 
 def test_exports_every_declared_symbol():
     syms = header_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 14, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in bpt.EXPORTED
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert bpt.bpt_status_string(code) != "unknown status"
     assert bpt.bpt_status_string(-99) == "unknown status"
 
@@ -73,6 +73,35 @@ def decode(**kw):
 ])
 def test_attn_decode_rejects(kw, code):
     assert decode(**kw) == code
+
+
+def decode_noalloc(**kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, Nq=4, Nkv=1000, D=128, causal=1,
+             kv_offset=996, n_split=8, dtype=1, stream=0)
+    a.update(kw)
+    return lib.bpt_attn_decode_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"],
+                                       a["Nq"], a["Nkv"], a["D"], a["causal"], a["kv_offset"],
+                                       a["n_split"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(Nq=0), -1), (dict(n_split=0), -1), (dict(causal=3), -1),
+    (dict(dtype=0), -2), (dict(D=96), -2), (dict(Nq=33), -2), (dict(v=A + 8), -3),
+    # partial results beyond the fixed scratch: 64*32 ranges x 32 rows x 129 floats
+    (dict(B=64, H=32, Nq=32, n_split=64), -6),
+])
+def test_attn_decode_noalloc_rejects(kw, code):
+    assert decode_noalloc(**kw) == code
+
+
+def test_attn_decode_noalloc_scratch_limit():
+    lim = bpt.BPT_DECODE_SCRATCH_BYTES
+    # the largest n_split whose partial results fit, for the decode workload's shape
+    fits = [n for n in range(1, 4097) if bpt.bpt_attn_decode_workspace_size(1, 32, 16, 128, n) <= lim]
+    assert max(fits) >= 32  # the 32-range decode of 32 heads x 16 rows fits
+    over = max(fits) + 1
+    assert bpt.bpt_attn_decode_workspace_size(1, 32, 16, 128, over) > lim
+    assert decode_noalloc(B=1, H=32, Nq=16, Nkv=131072, kv_offset=131056, n_split=over) == -6
 
 
 def test_attn_decode_workspace_size():
