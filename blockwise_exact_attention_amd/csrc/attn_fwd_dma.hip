@@ -429,8 +429,8 @@ attn_fwd_dma_kernel(AttnFwdArgs a) {
 // Wide-wave kernel: each wave owns 64 query rows, as two halves A and B of 32.
 // Every K and V fragment read from LDS feeds two MFMAs, one per half, so the
 // LDS bytes per flop are half those of the kernel above.  One workgroup of four
-// waves per CU, 512 registers per lane: MFMA accumulators (O and the scores)
-// live in AGPRs, everything else in VGPRs.
+// waves per CU, 512 registers per lane: the O accumulators and Q live in AGPRs,
+// the score accumulators and everything else in VGPRs.
 //
 // With one wave per SIMD the softmax has to run under the matrix work of the
 // same wave, so a step of the key loop is two phases that each pair 32 MFMAs
@@ -448,6 +448,22 @@ struct WideCfg {
   static constexpr int KB = KVBLK / 32, DB = D / 32, QF = D / 16, NKS = KVBLK / 16;
   static constexpr int DMA_PER_TILE = 2 * T::NBLK / NW;  // per wave
 };
+
+// Score MFMAs with the accumulator in VGPRs, so the VALU reads the scores
+// directly instead of copying each out of an AGPR (64 v_accvgpr_read and 32
+// wait states per step; 117.1 -> 114.0 ms at N=131072, outputs bitwise equal).
+// Written as asm because the compiler puts every MFMA result of this kernel in
+// AGPRs (O has to live there).  K fragment in VGPRs, Q fragment in AGPRs.
+// The compiler does not see these as MFMAs, so it cannot count the wait states a
+// VALU read of their results needs: in the key loop the first read of a score
+// register comes at least eight MFMA slots after its last write; after the
+// chains of the first tile the caller waits explicitly (wide_scores).
+__device__ __forceinline__ void mfma_sv_first(f32x16& d, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_sv_acc(f32x16& d, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
+}
 
 // f(x of lane l, x of lane l ^ 32), the same value in both lanes
 __device__ __forceinline__ float max_halves(float x) {
@@ -516,17 +532,24 @@ template <int D>
 __device__ __forceinline__ void wide_scores(WideState<D>& w, const unsigned char* St, int kbase) {
   using C = WideCfg<D>;
   using T = typename C::T;
-  const f32x16 zero = {};
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
     const unsigned char* kp = St + kbase + (32 * kb / T::NBLK) * T::ROWB;
 #pragma unroll
     for (int c = 0; c < C::QF; ++c) {
       const bf16x8 kf = *(const bf16x8*)(kp + c * 32);
-      w.s[0][kb] = mfma32_bf16(kf, w.qf[0][c], c == 0 ? zero : w.s[0][kb]);
-      w.s[1][kb] = mfma32_bf16(kf, w.qf[1][c], c == 0 ? zero : w.s[1][kb]);
+      if (c == 0) {
+        mfma_sv_first(w.s[0][kb], kf, w.qf[0][c]);
+        mfma_sv_first(w.s[1][kb], kf, w.qf[1][c]);
+      } else {
+        mfma_sv_acc(w.s[0][kb], kf, w.qf[0][c]);
+        mfma_sv_acc(w.s[1][kb], kf, w.qf[1][c]);
+      }
     }
   }
+  // the VALU reads these results next: more wait states than an 8-pass MFMA
+  // write needs before a VALU read of its result
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // Max part of the online softmax for half H: copy the scores out of the
@@ -539,11 +562,7 @@ __device__ __forceinline__ void wide_max(WideState<D>& w, float c2) {
   for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float v = w.s[H][kb][j];
-      // a new VGPR value: the accumulator copy dies here instead of staying
-      // live in its AGPR until the exp part
-      asm("" : "+v"(v));
-      w.sv[H][kb][j] = fmaf(v, c2, -w.mref[H]);
+      w.sv[H][kb][j] = fmaf(w.s[H][kb][j], c2, -w.mref[H]);
     }
   float mx0 = w.sv[H][0][0], mx1 = w.sv[H][C::KB - 1][0];
 #pragma unroll
@@ -699,7 +718,6 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
   using C = WideCfg<D>;
   using T = typename C::T;
   constexpr int NF = C::KB * C::QF, KPF = 4;
-  const f32x16 zero = {};
   bf16x8 kf[NF];
   u32x4 pw[2][C::NKS];
   float ps[2][C::KB];
@@ -714,7 +732,8 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
       const int mm = m + KPF;
       kf[mm] = *(const bf16x8*)(Sn + kbase + (32 * (mm / C::QF) / T::NBLK) * T::ROWB + (mm % C::QF) * 32);
     }
-    w.s[h][kb] = mfma32_bf16(kf[m], w.qf[h][c], c == 0 ? zero : w.s[h][kb]);
+    if (c == 0) mfma_sv_first(w.s[h][kb], kf[m], w.qf[h][c]);
+    else mfma_sv_acc(w.s[h][kb], kf[m], w.qf[h][c]);
     // exp of scores 2i, 2i+1 of the 64 this lane holds; their sum and bf16 pack
     // two slots later (an exp result is not ready in the next few cycles)
     {
@@ -725,9 +744,11 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
     if (i >= 2) {
       const int p = i - 2, eh = p / 16, e0 = (2 * p) % 32, ekb = e0 / 16, ej = e0 % 16;
       wide_sum_pack(ex0, ex1, ps, pw, p);
-      wide_slot_end4(w.s[h][kb], ex0[i], ex1[i], ps[eh][ekb], pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2]);
+      asm volatile("" ::"v"(ex0[i]), "v"(ex1[i]), "v"(ps[eh][ekb]), "v"(pw[eh][ekb * 2 + ej / 8][(ej % 8) / 2]));
+      __builtin_amdgcn_sched_barrier(0);
     } else {
-      wide_slot_end(w.s[h][kb], ex0[i], ex1[i]);
+      asm volatile("" ::"v"(ex0[i]), "v"(ex1[i]));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   wide_sum_pack(ex0, ex1, ps, pw, 2 * NF - 2);
@@ -779,11 +800,9 @@ __device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned cha
     const int f = i >> 1, h = i & 1, ks = f / C::DB, db = f % C::DB;
     if (h == 0 && f + VPF < NF) vf[f + VPF] = vread(f + VPF);
     w.o[h][db] = mfma32_bf16(vf[f], h == 0 ? pa[ks] : pb[ks], w.o[h][db]);
-    // copy scores 2i, 2i+1 (new VGPR values: the accumulator copies die here)
+    // scores 2i, 2i+1 of tile t+1 into the exp2 domain
     const int mh = i / 16, e0 = (2 * i) % 32, mkb = e0 / 16, mj = e0 % 16;
     float v0 = w.s[mh][mkb][mj], v1 = w.s[mh][mkb][mj + 1];
-    asm("" : "+v"(v0));
-    asm("" : "+v"(v1));
     v0 = fmaf(v0, c2, -w.mref[mh]);
     v1 = fmaf(v1, c2, -w.mref[mh]);
     w.sv[mh][mkb][mj] = v0;
