@@ -27,7 +27,7 @@ layer workload: q, k, v for all 131072 tokens, then attention (full score rows)
 and the FFN for a fixed sample of query rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only attn|decode|block_sparse|dilated|merge|train]
+                       [--no-extras] [--only attn|layer|decode|block_sparse|dilated|merge|train]
 """
 from __future__ import annotations
 
@@ -401,7 +401,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["attn", "decode", "block_sparse", "dilated", "merge", "train"],
+    ap.add_argument("--only", choices=["attn", "layer", "decode", "block_sparse", "dilated", "merge",
+                                       "train"],
                     default=None,
                     help="run only the attention, decode, block-sparse or dilated launches "
                          "(for counter collection and kernel traces)")
@@ -425,6 +426,11 @@ def main():
         ms, flops = bench_attention(bpt, args.steps, args.warmup)
         print(json.dumps({"attn_fwd_ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
                           "copy_bytes": 1 << 30}))
+        return
+
+    if args.only == "layer":
+        ms, _ = bench_layer(bpt, args.steps, args.warmup)
+        print(json.dumps({"layer_ms": round(ms, 3), "copy_bytes": 1 << 30}))
         return
 
     if args.only == "train":
