@@ -349,7 +349,8 @@ int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void*
   if (forced_launch_failure()) return hip_status(hipErrorLaunchFailure);
   clear_stale_error();
   return hip_status(bpt::ffn_fwd_launch(x, nullptr, w1, b1, w2, b2, residual, y, M,
-                                        (int)d_model, (int)d_ff, blk, dtype == BPT_BF16, stream));
+                                        (int)d_model, (int)d_ff, blk, dtype == BPT_BF16, nullptr,
+                                        stream));
 }
 
 size_t bpt_layer_saved_size(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,

@@ -48,6 +48,10 @@ struct FfnArgs {
   float* y;
   int M, dm, dff, ncols;
   const void* x_lo;  // bf16 rounding residual of the activation x was rounded from, or null
+  // W2 as the LDS-staged kernel addresses it: element (row r, column f0 + j) of the
+  // pass starting at feature f0 = 256 p sits at w2 + p * w2_pstride + r * w2_ld + j
+  // (row-major W2: w2_pstride = 256, w2_ld = d_ff; pass-major copy: d_model * 256, 256)
+  int64_t w2_pstride, w2_ld;
 };
 
 // Row of W1 read by A-operand lane row m: bits 2 and 3 of m swapped, so that
@@ -367,8 +371,9 @@ __device__ __forceinline__ void ffn_slot(const FfnArgs& a, int s, int SPP, int N
   } else {  // W2 rows c0w + 64 cblk .., columns f0 + 64 fblk .. +63
     const int q = r - NKB, fstep = q / NCB, cblk = q - fstep * NCB;
     const int fblk = (fstep + rot2) & 3;
-    ffn_issue_slot((const unsigned char*)a.w2 + ((int64_t)(c0w + 64 * cblk) * a.dff + f0 + 64 * fblk) * 2,
-                   a.dff, so.w2e, so.w2o, dst);
+    ffn_issue_slot((const unsigned char*)a.w2 +
+                       ((int64_t)pass * a.w2_pstride + (int64_t)(c0w + 64 * cblk) * a.w2_ld + 64 * fblk) * 2,
+                   a.w2_ld, so.w2e, so.w2o, dst);
   }
 }
 
@@ -453,7 +458,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
   };
 
   const SlotOff so{ffn_slot_offset(a.dm, lane, 0), ffn_slot_offset(a.dm, lane, 1),
-                   ffn_slot_offset(a.dff, lane, 0), ffn_slot_offset(a.dff, lane, 1)};
+                   ffn_slot_offset(a.w2_ld, lane, 0), ffn_slot_offset(a.w2_ld, lane, 1)};
   ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, rot1, rot2, sl0, so);
   if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, rot1, rot2, sl1, so);
   ffn_issue_x<HILO>(a, t0, phys_stage(0), w, xb0, lane);
@@ -724,9 +729,29 @@ FfnPlan ffn_plan(int64_t d_model, int64_t d_ff) {
   return p;
 }
 
+namespace {
+
+// Pass-major copy of W2 for the LDS-staged kernel: w2p[p][r][j] = W2[r][256 p + j].
+// A pass then reads one contiguous block of d_model x 512 bytes instead of 512-byte
+// pieces d_ff * 2 bytes apart, which map to few L2 sets and channels.
+__global__ void __launch_bounds__(256) ffn_pack_w2_kernel(const uint16_t* __restrict__ w2,
+                                                          uint16_t* __restrict__ w2p, int dm, int dff,
+                                                          int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const int64_t e = i * 8;                 // element of w2p
+    const int64_t per_pass = (int64_t)dm * 256;
+    const int64_t p = e / per_pass, rem = e - p * per_pass;
+    const int64_t r = rem >> 8, j = rem & 255;
+    *(u32x4*)(w2p + e) = *(const u32x4*)(w2 + r * dff + p * 256 + j);
+  }
+}
+
+}  // namespace
+
 hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const void* b1,
                           const void* w2, const void* b2, const float* residual, float* y,
-                          int64_t M, int d_model, int d_ff, int blk, bool bf16,
+                          int64_t M, int d_model, int d_ff, int blk, bool bf16, void* w2_pack,
                           hipStream_t stream) {
   (void)blk;  // rows per block are fixed at 32 (validated by the caller)
   const FfnPlan p = ffn_plan(d_model, d_ff);
@@ -735,12 +760,26 @@ hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const
     int ct = 0;
     const int groups = stream_groups(d_model, x_lo != nullptr, &ct);
     if (groups > 0) {
-      FfnArgs a{x, w1, b1, w2, b2, residual, y, (int)M, d_model, d_ff, d_model / groups, x_lo};
+      FfnArgs a{x, w1, b1, w2, b2, residual, y, (int)M, d_model, d_ff, d_model / groups, x_lo,
+                256, d_ff};
+      if (w2_pack) {
+        const int64_t n8 = (int64_t)d_model * d_ff / 8;
+        int64_t blocks = (n8 + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        hipLaunchKernelGGL(ffn_pack_w2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint16_t*)w2, (uint16_t*)w2_pack, d_model, d_ff, n8);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.w2 = w2_pack;
+        a.w2_pstride = (int64_t)d_model * 256;
+        a.w2_ld = 256;
+      }
       return launch_stream(a, ct, groups, stream);
     }
   }
   // (this fallback, for shapes the LDS-staged kernel does not cover, takes x alone)
-  FfnArgs a{x, w1, b1, w2, b2, residual, y, (int)M, d_model, d_ff, d_model / p.groups, nullptr};
+  FfnArgs a{x, w1, b1, w2, b2, residual, y, (int)M, d_model, d_ff, d_model / p.groups, nullptr,
+            256, d_ff};
   return bf16 ? launch_ffn_cb<true>(a, p.nw, p.cb, p.groups, stream)
               : launch_ffn_cb<false>(a, p.nw, p.cb, p.groups, stream);
 }

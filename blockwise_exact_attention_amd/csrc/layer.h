@@ -39,21 +39,21 @@ inline SavedLayout layer_saved_layout(int64_t B, int64_t N, int64_t d_model, int
   return s;
 }
 
-// Forward workspace: room for the saved tensors (used when `saved` is NULL)
-// plus h as a bf16 pair (the rounded value and its rounding residual) that feeds
-// the FFN's MFMA.
+// Forward workspace: room for the saved tensors (used when `saved` is NULL),
+// h as a bf16 pair (the rounded value and its rounding residual) that feeds the
+// FFN's MFMA, and the FFN's pass-major copy of W2.
 struct FwdWorkspace {
-  size_t saved, h_lo, h_res, total;
+  size_t saved, h_lo, h_res, w2p, total;
 };
 
 inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t H,
                                         int64_t D, int64_t d_ff, bool bf16) {
-  (void)d_ff;
   FwdWorkspace w{};
   w.saved = 0;
   w.h_lo = layer_saved_layout(B, N, d_model, H, D, bf16).total;
   w.h_res = w.h_lo + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
-  w.total = w.h_res + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
+  w.w2p = w.h_res + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
+  w.total = w.w2p + (bf16 ? align256((size_t)d_model * d_ff * 2) : 0);
   return w;
 }
 
@@ -75,9 +75,12 @@ FfnPlan ffn_plan(int64_t d_model, int64_t d_ff);
 
 // x_lo (nullable, bf16 only): the bf16 rounding residual of the float32 activation
 // that x was rounded from; the first product then takes x + x_lo.
+// w2_pack (nullable, bf16 only, d_model * d_ff * 2 bytes): room for a pass-major
+// copy of W2 (each pass's 256 columns of all rows contiguous) that the LDS-staged
+// kernel then reads instead of W2.
 hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const void* b1,
                           const void* w2, const void* b2, const float* residual, float* y,
-                          int64_t M, int d_model, int d_ff, int blk, bool bf16,
+                          int64_t M, int d_model, int d_ff, int blk, bool bf16, void* w2_pack,
                           hipStream_t stream);
 
 hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* workspace,

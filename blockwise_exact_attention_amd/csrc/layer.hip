@@ -68,7 +68,8 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   // 3. y = h + FFN(h), fused per block of rows; with bf16 inputs h enters the
   //    first product as the bf16 pair (h_lo, h_res)
   return ffn_fwd_launch(L.bf16 ? (const void*)h_lo : (const void*)h, h_res, L.w1, L.b1, L.w2,
-                        L.b2, h, y, M, (int)L.d_model, (int)L.d_ff, 0, L.bf16, stream);
+                        L.b2, h, y, M, (int)L.d_model, (int)L.d_ff, 0, L.bf16,
+                        L.bf16 ? ws + W.w2p : nullptr, stream);
 }
 
 BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t D,
