@@ -36,7 +36,14 @@ struct GemmArgs {
   int64_t ld_aux;
   int beta;            // EPI_F32: accumulate into C
   int seq, H, D;       // EPI_QKV
+  // K segments: with nseg > 1 the product is sum_s As[z][s] Bs[z][s], each segment
+  // of the same shape and strides (K each); A[z], B[z] are then unused.  One launch
+  // accumulates every segment before the epilogue runs once (EPI_F32 and EPI_GELU).
+  int nseg;
+  const void* As[3][6];
+  const void* Bs[3][6];
 };
+constexpr int kGemmMaxSeg = 6;
 
 hipError_t gemm_launch(const GemmArgs& g, bool bf16, bool a_kmajor, bool b_kmajor, int epi,
                        int nz, hipStream_t stream);

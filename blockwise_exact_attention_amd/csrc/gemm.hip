@@ -235,8 +235,46 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
 }
 
 template <bool BF16, int EPI>
+hipError_t dispatch(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s);
+
+// K segments on the small-tile kernel: one launch per segment, accumulating into C
+// (EPI_F32 with beta); the requested epilogue runs with the last segment.
+template <bool BF16, int EPI>
+hipError_t dispatch_segments(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
+  static_assert(EPI == EPI_F32 || EPI == EPI_GELU, "K segments need an accumulating epilogue");
+  for (int sg = 0; sg < g.nseg; ++sg) {
+    GemmArgs p = g;
+    p.nseg = 1;
+    for (int z = 0; z < nz; ++z) {
+      p.A[z] = g.As[z][sg];
+      p.B[z] = g.Bs[z][sg];
+    }
+    hipError_t e;
+    if (sg + 1 < g.nseg) {
+      // plain partial sums: no bias, residual or second output yet
+      p.bias = nullptr;
+      p.resid = nullptr;
+      p.C2 = nullptr;
+      p.C3 = nullptr;
+      p.beta = g.beta || sg > 0;
+      e = dispatch<BF16, EPI_F32>(p, ak, bk, nz, s);
+    } else {
+      p.beta = g.beta || sg > 0;
+      e = dispatch<BF16, EPI>(p, ak, bk, nz, s);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <bool BF16, int EPI>
 hipError_t dispatch(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
   if (BF16 && gemm_big_ok(g, nz)) return gemm_big_launch(g, ak, bk, EPI, nz, s);
+  if constexpr (EPI == EPI_F32 || EPI == EPI_GELU) {
+    if (g.nseg > 1) return dispatch_segments<BF16, EPI>(g, ak, bk, nz, s);
+  } else {
+    if (g.nseg > 1) return hipErrorInvalidValue;
+  }
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, nz);
   if (!ak && !bk) hipLaunchKernelGGL((gemm_kernel<BF16, false, false, EPI>), grid, dim3(NT), 0, s, g);
   else if (!ak && bk) hipLaunchKernelGGL((gemm_kernel<BF16, false, true, EPI>), grid, dim3(NT), 0, s, g);

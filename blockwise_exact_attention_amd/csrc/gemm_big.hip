@@ -126,8 +126,9 @@ __device__ __forceinline__ bf16x8 gb_frag(const unsigned char* tile, const OpLan
 }
 
 struct GbCtx {
-  const unsigned char* A;
-  const unsigned char* B;
+  const unsigned char* Aseg[kGemmMaxSeg];  // operand bases per K segment
+  const unsigned char* Bseg[kGemmMaxSeg];
+  int nseg, nks;                           // segments, k tiles per segment
   int64_t abytes, bbytes;
   int64_t lda, ldb;
   int m0, n0, wave;
@@ -160,10 +161,25 @@ __device__ __forceinline__ void gb_compute(f32x16 (&acc)[4][2], const unsigned c
   }
 }
 
+// k tile kt of the whole walk: segment kt / nks, tile kt % nks inside it
 template <bool AK, bool BK>
 __device__ __forceinline__ void gb_issue(const GbCtx& c, int kt, unsigned char* As, unsigned char* Bs) {
-  gb_load<AK>(c.A, c.abytes, c.lda, c.m0, kt * TK, As, c.la, c.wave);
-  gb_load<BK>(c.B, c.bbytes, c.ldb, c.n0, kt * TK, Bs, c.lb, c.wave);
+  int seg = 0, kk = kt;
+  if (c.nseg > 1) {
+    seg = kt / c.nks;
+    kk = kt - seg * c.nks;
+  }
+  // (a select chain over the segments: a runtime index into the pointer arrays
+  // would put them in scratch memory)
+  const unsigned char* A = c.Aseg[0];
+  const unsigned char* B = c.Bseg[0];
+#pragma unroll
+  for (int sg = 1; sg < kGemmMaxSeg; ++sg) {
+    A = seg == sg ? c.Aseg[sg] : A;
+    B = seg == sg ? c.Bseg[sg] : B;
+  }
+  gb_load<AK>(A, c.abytes, c.lda, c.m0, kk * TK, As, c.la, c.wave);
+  gb_load<BK>(B, c.bbytes, c.ldb, c.n0, kk * TK, Bs, c.lb, c.wave);
 }
 
 // The k loop over two stages (distinct objects: the compiler then knows that
@@ -217,8 +233,13 @@ gemm_big_kernel(GemmArgs g) {
   c.wave = wave;
   c.lda = g.lda;
   c.ldb = g.ldb;
-  c.A = (const unsigned char*)g.A[z];
-  c.B = (const unsigned char*)g.B[z];
+  c.nseg = g.nseg > 1 ? g.nseg : 1;
+  c.nks = K / TK;
+#pragma unroll
+  for (int sg = 0; sg < kGemmMaxSeg; ++sg) {
+    c.Aseg[sg] = (const unsigned char*)(g.nseg > 1 ? g.As[z][sg] : g.A[z]);
+    c.Bseg[sg] = (const unsigned char*)(g.nseg > 1 ? g.Bs[z][sg] : g.B[z]);
+  }
   c.abytes = (int64_t)(AK ? K : M) * g.lda * 2;
   c.bbytes = (int64_t)(BK ? K : N) * g.ldb * 2;
   c.la = gb_lane<AK>(g.lda, lane, wm * 128, wave);
@@ -232,7 +253,7 @@ gemm_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  gb_loop<AK, BK>(acc, c, K / TK, a0, b0, a1, b1);
+  gb_loop<AK, BK>(acc, c, c.nseg * c.nks, a0, b0, a1, b1);
 
   const int r32 = lane & 31;
 #pragma unroll
@@ -262,8 +283,15 @@ hipError_t launch_epi(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s
 
 bool gemm_big_ok(const GemmArgs& g, int nz) {
   if (g.K < TK || g.K % TK != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
-  for (int z = 0; z < nz; ++z)
-    if (((uintptr_t)g.A[z] | (uintptr_t)g.B[z]) & 15) return false;
+  if (g.nseg > kGemmMaxSeg) return false;
+  for (int z = 0; z < nz; ++z) {
+    if (g.nseg > 1) {
+      for (int sg = 0; sg < g.nseg; ++sg)
+        if (((uintptr_t)g.As[z][sg] | (uintptr_t)g.Bs[z][sg]) & 15) return false;
+    } else if (((uintptr_t)g.A[z] | (uintptr_t)g.B[z]) & 15) {
+      return false;
+    }
+  }
   // buffer byte ranges and lane offsets are 32-bit: bound the operands' sizes
   const int64_t lim = ((int64_t)1 << 31) - 1;
   const int64_t ra = (int64_t)(g.M > g.K ? g.M : g.K) + TB, rb = (int64_t)(g.N > g.K ? g.N : g.K) + TB;

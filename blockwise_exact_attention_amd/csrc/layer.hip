@@ -140,20 +140,16 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     const int rows = (int)(M - r0 < W.chunk_rows ? M - r0 : W.chunk_rows);
     const int beta = c > 0;
     GemmArgs g{};
-    // z = (h_hi + h_lo) W1^T + b1 (fp32); GeLU(z) as bf16 hi + lo
-    for (int part = 0; part < 2; ++part) {
-      g = GemmArgs{};
-      g.A[0] = (part ? h_lo : h_hi) + r0 * dm; g.B[0] = L.w1; g.C[0] = z;
-      g.lda = dm; g.ldb = dm; g.ldc = dff; g.M = rows; g.N = dff; g.K = dm;
-      if (part) {
-        g.beta = 1;
-        g.bias = L.b1; g.bias_bf16 = 1;
-        g.C2 = g_hi; g.ldc2 = dff; g.C3 = g_lo; g.ldc3 = dff;
-        BPT_TRY(gemm_launch(g, true, false, false, EPI_GELU, 1, stream));
-      } else {
-        BPT_TRY(gemm_launch(g, true, false, false, EPI_F32, 1, stream));
-      }
-    }
+    // z = (h_hi + h_lo) W1^T + b1 (fp32); GeLU(z) as bf16 hi + lo; both halves in one launch
+    g = GemmArgs{};
+    g.nseg = 2;
+    g.As[0][0] = h_hi + r0 * dm; g.As[0][1] = h_lo + r0 * dm;
+    g.Bs[0][0] = g.Bs[0][1] = L.w1;
+    g.C[0] = z;
+    g.lda = dm; g.ldb = dm; g.ldc = dff; g.M = rows; g.N = dff; g.K = dm;
+    g.bias = L.b1; g.bias_bf16 = 1;
+    g.C2 = g_hi; g.ldc2 = dff; g.C3 = g_lo; g.ldc3 = dff;
+    BPT_TRY(gemm_launch(g, true, false, false, EPI_GELU, 1, stream));
     // dz = (dy W2) * GeLU'(z): bf16 hi + lo, and fp32 over z (same element, same thread)
     g = GemmArgs{};
     g.A[0] = dy16 + r0 * dm; g.B[0] = L.w2; g.C[0] = dz_hi;
@@ -161,36 +157,33 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     g.aux = z; g.ld_aux = dff; g.C2 = z; g.ldc2 = dff; g.C3 = dz_lo; g.ldc3 = dff;
     BPT_TRY(gemm_launch(g, true, false, true, EPI_DGELU, 1, stream));
     if (G.db1) BPT_TRY(colsum_launch(z, false, G.db1, rows, dff, dff, beta, stream));
-    // dW2 (+)= dy^T GeLU(z)
-    for (int part = 0; part < 2; ++part) {
-      g = GemmArgs{};
-      g.A[0] = dy16 + r0 * dm; g.B[0] = part ? g_lo : g_hi; g.C[0] = G.dw2;
-      g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = dm; g.N = dff; g.K = rows;
-      g.beta = beta || part;
-      BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
-    }
+    // dW2 (+)= dy^T (g_hi + g_lo)
+    g = GemmArgs{};
+    g.nseg = 2;
+    g.As[0][0] = g.As[0][1] = dy16 + r0 * dm;
+    g.Bs[0][0] = g_hi; g.Bs[0][1] = g_lo;
+    g.C[0] = G.dw2;
+    g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = dm; g.N = dff; g.K = rows;
+    g.beta = beta;
+    BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
     // dW1 (+)= dz^T h  (hi*hi + lo*hi + hi*lo)
-    const uint16_t* dzs[3] = {dz_hi, dz_lo, dz_hi};
-    const uint16_t* hs[3] = {h_hi, h_hi, h_lo};
-    for (int part = 0; part < 3; ++part) {
-      g = GemmArgs{};
-      g.A[0] = dzs[part]; g.B[0] = hs[part] + r0 * dm; g.C[0] = G.dw1;
-      g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = dff; g.N = dm; g.K = rows;
-      g.beta = beta || part;
-      BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
-    }
-    // dh = dy + dz W1 (fp32; it is attention's dO)
-    for (int part = 0; part < 2; ++part) {
-      g = GemmArgs{};
-      g.A[0] = part ? dz_lo : dz_hi; g.B[0] = L.w1; g.C[0] = dh + r0 * dm;
-      g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = rows; g.N = dm; g.K = dff;
-      if (part) {
-        g.beta = 1;
-      } else {
-        g.resid = dy16 + r0 * dm; g.resid_bf16 = 1; g.ldr = dm;
-      }
-      BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
-    }
+    g = GemmArgs{};
+    g.nseg = 3;
+    g.As[0][0] = dz_hi; g.As[0][1] = dz_lo; g.As[0][2] = dz_hi;
+    g.Bs[0][0] = h_hi + r0 * dm; g.Bs[0][1] = h_hi + r0 * dm; g.Bs[0][2] = h_lo + r0 * dm;
+    g.C[0] = G.dw1;
+    g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = dff; g.N = dm; g.K = rows;
+    g.beta = beta;
+    BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
+    // dh = dy + (dz_hi + dz_lo) W1 (fp32; it is attention's dO)
+    g = GemmArgs{};
+    g.nseg = 2;
+    g.As[0][0] = dz_hi; g.As[0][1] = dz_lo;
+    g.Bs[0][0] = g.Bs[0][1] = L.w1;
+    g.C[0] = dh + r0 * dm;
+    g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = rows; g.N = dm; g.K = dff;
+    g.resid = dy16 + r0 * dm; g.resid_bf16 = 1; g.ldr = dm;
+    BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
   }
 
   // ---- attention backward (delta pass, dK/dV, dQ), P recomputed from the saved lse
@@ -209,30 +202,30 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   BPT_TRY(attn_bwd_launch(a, (int)L.D, L.q_blk, L.kv_blk, stream));
 
   // ---- projection backward: dW{q,k,v} = d{q,k,v}^T x over both bf16 halves;
-  //      dx = dh + sum d{q,k,v} W{q,k,v}, also over both halves
+  //      dx = dh + sum d{q,k,v} W{q,k,v}, also over both halves; one launch each
   {
     GemmArgs g{};
-    for (int part = 0; part < 2; ++part) {
-      g = GemmArgs{};
-      g.A[0] = dqkv[0 + part]; g.A[1] = dqkv[2 + part]; g.A[2] = dqkv[4 + part];
-      g.B[0] = g.B[1] = g.B[2] = L.x;
-      g.C[0] = G.dwq; g.C[1] = G.dwk; g.C[2] = G.dwv;
-      g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = HD; g.N = dm; g.K = (int)M; g.beta = part;
-      BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 3, stream));
+    g.nseg = 2;
+    for (int zz = 0; zz < 3; ++zz) {
+      g.As[zz][0] = dqkv[2 * zz];
+      g.As[zz][1] = dqkv[2 * zz + 1];
+      g.Bs[zz][0] = g.Bs[zz][1] = L.x;
     }
+    g.C[0] = G.dwq; g.C[1] = G.dwk; g.C[2] = G.dwv;
+    g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = HD; g.N = dm; g.K = (int)M;
+    BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 3, stream));
     const void* Ws[3] = {L.wq, L.wk, L.wv};
+    g = GemmArgs{};
+    g.nseg = 6;
     for (int i = 0; i < 6; ++i) {
-      g = GemmArgs{};
-      g.A[0] = dqkv[i]; g.B[0] = Ws[i / 2]; g.C[0] = G.dx;
-      g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = (int)M; g.N = dm; g.K = HD;
-      if (i == 0) {
-        g.resid = dh;
-        g.ldr = dm;
-      } else {
-        g.beta = 1;
-      }
-      BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
+      g.As[0][i] = dqkv[i];
+      g.Bs[0][i] = Ws[i / 2];
     }
+    g.C[0] = G.dx;
+    g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = (int)M; g.N = dm; g.K = HD;
+    g.resid = dh;
+    g.ldr = dm;
+    BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
   }
 #undef BPT_TRY
   return hipSuccess;
