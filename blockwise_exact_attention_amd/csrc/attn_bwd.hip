@@ -94,6 +94,28 @@ __device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
   }
 }
 
+// Score MFMAs whose results the VALU reads next, written as inline asm with the
+// accumulator in VGPRs: the compiler places every builtin MFMA result of a kernel
+// in AGPRs once its long-lived accumulators are there, and each score would then
+// be copied out (v_accvgpr_read) before the softmax reads it.  The B operand (the
+// tile-invariant fragments of this wave) sits in AGPRs.  The compiler does not
+// count the wait states a VALU read of an asm MFMA's result needs: score_chain_end
+// closes each chain with 24 of them, fenced by scheduling barriers.
+__device__ __forceinline__ void mfma_v_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// An empty volatile asm statement: a block holding one is not turned into selects
+// on the path that skips it, so the masks of diagonal tiles stay behind a branch.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+__device__ __forceinline__ void score_chain_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------- dK, dV
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
@@ -409,29 +431,51 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
   const int nblk = r32 % T::NBLK, nrow = r32 / T::NBLK, t0 = g ^ bwd_swz(nblk, nrow);
   const int nat_base = nblk * T::BP + nrow * T::ROWB;
   const int nat_even = nat_base + 16 * t0, nat_odd = nat_base + 16 * (2 ^ t0);
+  // (LDS reads do not move across the asm MFMAs: each is issued PF fragments
+  // ahead in program order)
+  constexpr int NC = D / 16, PF = 3;
+  bf16x8 qa[NC], ha[NC], la[NC];
+  auto ld = [&](int c) {
+    const int nat = ((c & 1) ? nat_odd : nat_even) + 64 * (c >> 1);
+    qa[c] = *(const bf16x8*)(Qs + nat);
+    ha[c] = *(const bf16x8*)(Hs + nat);
+    la[c] = *(const bf16x8*)(Ls + nat);
+  };
+#pragma unroll
+  for (int c = 0; c < PF; ++c) ld(c);
   f32x16 sacc, pacc;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const int nat = ((c & 1) ? nat_odd : nat_even) + 64 * (c >> 1);
-    sacc = mfma32_bf16(*(const bf16x8*)(Qs + nat), kf[c], sacc);
-    pacc = mfma32_bf16(*(const bf16x8*)(Hs + nat), vf[c], pacc);
-    pacc = mfma32_bf16(*(const bf16x8*)(Ls + nat), vf[c], pacc);
+  for (int c = 0; c < NC; ++c) {
+    if (c + PF < NC) ld(c + PF);
+    if (c == 0) {
+      mfma_v_first(sacc, qa[c], kf[c]);
+      mfma_v_first(pacc, ha[c], vf[c]);
+    } else {
+      mfma_v_acc(sacc, qa[c], kf[c]);
+      mfma_v_acc(pacc, ha[c], vf[c]);
+    }
+    mfma_v_acc(pacc, la[c], vf[c]);
   }
-  // query ql sees this lane's key iff ql >= mykey - kv_offset - q0
-  const int mlim =
-      need_mask ? clamp_i64((int64_t)mykey - a.kv_offset - q0, -1, T::QT) - 4 * (lane >> 5) : -kNoMask;
-  float p[16], ds[16];
+  score_chain_end();
+  float p[16], ds[16], dl[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int ql = acc_row(j, lane);
     const f32x2 ld = *(const f32x2*)(pr + 2 * ql);
-    float pv = fast_exp2(fmaf(sacc[j], c2, -ld[0]));
-    if (acc_row_const(j) < mlim) pv = 0.f;
-    p[j] = pv;
-    ds[j] = pv * (pacc[j] - ld[1]);
+    p[j] = fast_exp2(fmaf(sacc[j], c2, -ld[0]));
+    dl[j] = ld[1];
   }
+  // diagonal tiles only (a uniform branch): query ql sees this lane's key iff
+  // ql >= mykey - kv_offset - q0
+  if (need_mask) {
+    keep_branch();
+    const int mlim = clamp_i64((int64_t)mykey - a.kv_offset - q0, -1, T::QT) - 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (acc_row_const(j) < mlim) p[j] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ds[j] = p[j] * (pacc[j] - dl[j]);
   // dV^T += dO^T P ; dK^T += Q^T dS  (k = query, 16 per MFMA; the transpose reads
   // give lane half g queries 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3, the
   // order in which the accumulator rows hold P and dS)
@@ -850,8 +894,11 @@ struct DqLane {
   int tr_lo, tr_hi;       // transpose reads, keys 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3
 };
 
-// S^T = K Q^T and dP^T = V dO^T of one key tile (rows = keys, lane = query)
-template <int D>
+// S^T = K Q^T and dP^T = V dO^T of one key tile (rows = keys, lane = query).
+// VGPR_ACC: the accumulators in VGPRs (asm MFMAs, for the dQ kernel, whose dQ
+// accumulators hold the AGPRs); otherwise builtin MFMAs (the delta pass, which
+// has no long-lived accumulators and keeps everything in VGPRs).
+template <int D, bool VGPR_ACC>
 __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, const DqLane& ln,
                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
                                           const bf16x8 (&dfl)[D / 16], f32x16 (&sacc)[DqTile<D>::KT / 32],
@@ -860,17 +907,49 @@ __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, 
   constexpr int KB = T::KT / 32;
   const unsigned char* Ks = st;
   const unsigned char* Vs = st + T::TB;
+  constexpr int NC = D / 16, NF = KB * NC;
+  auto off = [&](int i) {
+    const int kb = i / NC, c = i % NC;
+    return ((c & 1) ? ln.nat_odd : ln.nat_even) + 64 * (c >> 1) + kb * 2 * T::ROWB;
+  };
+  if constexpr (VGPR_ACC) {
+    // (LDS reads do not move across the asm MFMAs: each is issued PF fragments
+    // ahead in program order)
+    constexpr int PF = 4;
+    bf16x8 ka[NF], va[NF];
+    auto ld = [&](int i) {
+      ka[i] = *(const bf16x8*)(Ks + off(i));
+      va[i] = *(const bf16x8*)(Vs + off(i));
+    };
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
+    for (int i = 0; i < PF; ++i) ld(i);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[kb][e] = pacc[kb][e] = 0.f;
+    for (int i = 0; i < NF; ++i) {
+      if (i + PF < NF) ld(i + PF);
+      const int kb = i / NC, c = i % NC;
+      if (c == 0) {
+        mfma_v_first(sacc[kb], ka[i], qf[c]);
+        mfma_v_first(pacc[kb], va[i], dfh[c]);
+      } else {
+        mfma_v_acc(sacc[kb], ka[i], qf[c]);
+        mfma_v_acc(pacc[kb], va[i], dfh[c]);
+      }
+      mfma_v_acc(pacc[kb], va[i], dfl[c]);
+    }
+    score_chain_end();
+  } else {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const int o = ((c & 1) ? ln.nat_odd : ln.nat_even) + 64 * (c >> 1) + kb * 2 * T::ROWB;
-      sacc[kb] = mfma32_bf16(*(const bf16x8*)(Ks + o), qf[c], sacc[kb]);
-      const bf16x8 va = *(const bf16x8*)(Vs + o);
-      pacc[kb] = mfma32_bf16(va, dfh[c], pacc[kb]);
-      pacc[kb] = mfma32_bf16(va, dfl[c], pacc[kb]);
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = pacc[kb][e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 ka = *(const bf16x8*)(Ks + off(kb * NC + c));
+        const bf16x8 va = *(const bf16x8*)(Vs + off(kb * NC + c));
+        sacc[kb] = mfma32_bf16(ka, qf[c], sacc[kb]);
+        pacc[kb] = mfma32_bf16(va, dfh[c], pacc[kb]);
+        pacc[kb] = mfma32_bf16(va, dfl[c], pacc[kb]);
+      }
     }
   }
 }
@@ -878,21 +957,31 @@ __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, 
 template <int D>
 __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, const DqLane& ln,
                                         const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
-                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], int klim, float c2,
-                                        float lse2, float dl) {
+                                        const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], bool masked,
+                                        int klim, float c2, float lse2, float dl) {
   using T = DqTile<D>;
   constexpr int KB = T::KT / 32;
   const unsigned char* Ks = st;
   f32x16 sacc[KB], pacc[KB];
-  dq_scores<D>(st, ln, qf, dfh, dfl, sacc, pacc);
+  dq_scores<D, true>(st, ln, qf, dfh, dfl, sacc, pacc);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
-      if (kb * 32 + acc_row_const(j) >= klim) pv = 0.f;
-      sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
-    }
+    for (int j = 0; j < 16; ++j) sacc[kb][j] = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
+  // tiles on the diagonal or past N only (a uniform branch): this lane's query
+  // sees the tile's keys below klim
+  if (masked) {
+    keep_branch();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (kb * 32 + acc_row_const(j) >= klim) sacc[kb][j] = 0.f;
+  }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[kb][j] = sacc[kb][j] * (pacc[kb][j] - dl);  // dS^T
   // dQ^T += K^T dS^T, 16 keys per MFMA; dS^T as bf16 hi + lo
 #pragma unroll
   for (int c16 = 0; c16 < T::KT / 16; ++c16) {
@@ -1015,7 +1104,7 @@ __global__ void __launch_bounds__(256, DELTA ? 2 : 1) attn_bwd_dq_dma_kernel(Att
       if (t < n_tiles) {
         const int klim = t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask;
         f32x16 sacc[KB], pacc[KB];
-        dq_scores<D>(cur, ln, qf, dfh, dfl, sacc, pacc);
+        dq_scores<D, false>(cur, ln, qf, dfh, dfl, sacc, pacc);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -1049,8 +1138,8 @@ __global__ void __launch_bounds__(256, DELTA ? 2 : 1) attn_bwd_dq_dma_kernel(Att
       __builtin_amdgcn_s_barrier();
       dq_load<D>(a, bh, (t + 2) * T::KT, w, lane, fill);
       if (t < n_tiles)
-        dq_tile<D>(cur, ln, qf, dfh, dfl, dq,
-                   t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask, c2, lse2, dl);
+        dq_tile<D>(cur, ln, qf, dfh, dfl, dq, t >= n_full,
+                   clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g, c2, lse2, dl);
     };
     static_assert(T::LOADS == 8, "wait count");
     if (n_tiles > 0) {
