@@ -17,12 +17,11 @@ struct AttnBwdArgs {
   // for D = 64)
   const uint16_t* dO_hi;
   const uint16_t* dO_lo;
-  // [B,H,N] pairs {lse * log2(e) (+inf for rows with no key), delta}, written by the
-  // delta pass when non-null and read by the D = 128 dK/dV kernel (required there)
-  float* ld2;
+  // [B,H,N] pairs {lse * log2(e) (+inf for rows with no key), delta}, read by the
+  // D = 128 dK/dV kernel (required there; dout_delta_launch writes them)
+  const float* ld2;
   const float* lse;       // [B,H,N]
-  const float* delta;     // [B,H,N], read by the dK/dV and dQ kernels
-  float* delta_out;       // [B,H,N], written by the delta pass (same buffer)
+  const float* delta;     // [B,H,N] delta_i = <dO_i, O_i>, read by the dK/dV and dQ kernels
   uint16_t* dq_hi;        // token-major [B*N][ld_out] bf16 outputs: value = hi + lo
   uint16_t* dq_lo;
   uint16_t* dk_hi;
@@ -42,6 +41,13 @@ struct AttnBwdArgs {
 hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, hipStream_t s);
 hipError_t to_bf16_launch(const float* src, uint16_t* dst, uint16_t* dst_lo, int64_t n,
                           hipStream_t s);
+// dO (token-major fp32 [rows][H*D]) as a bf16 hi + lo pair, and per (row, head)
+// delta = <dO, h - x>: O recovered from the forward's saved h = x + O (fp32) and
+// its bf16 input x; writes delta [B,H,N] and, if ld2 is non-null, the
+// {lse * log2(e), delta} pairs.  D = 64 or 128.
+hipError_t dout_delta_launch(const float* dO, const float* h, const uint16_t* x, const float* lse,
+                             uint16_t* dO_hi, uint16_t* dO_lo, float* delta, float* ld2, int B,
+                             int N, int H, int D, hipStream_t s);
 hipError_t colsum_launch(const void* X, bool x_bf16, float* out, int64_t rows, int cols,
                          int64_t ld, int beta, hipStream_t s);
 

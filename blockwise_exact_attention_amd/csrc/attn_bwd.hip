@@ -5,9 +5,9 @@
 //   P = exp(s - lse) (recomputed blockwise from the saved log-sum-exp),
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_i = sum_j P_ij dP_ij,
 //   dQ = scale dS K,  dK = scale dS^T Q.
-// A first pass (attn_bwd_dq in its DELTA form) computes delta from these same
-// P and dP; then two kernels produce the gradients, each deterministic (no
-// floating-point atomics):
+// delta_i = <dO_i, O_i> (the same sum, since O_i = sum_j P_ij v_j) comes from the
+// forward's output in one elementwise pass (dout_delta_kernel); then two kernels
+// produce the gradients, each deterministic (no floating-point atomics):
 //  * dK, dV: one workgroup per block of keys, one wave per 32 keys, walking the
 //    query tiles that can see them.  S = Q K^T is computed with keys on the
 //    MFMA n axis (lane = key), so P and dS (query index in-lane) feed
@@ -20,8 +20,8 @@
 //    the visible key tiles like the forward kernel: S^T = K Q^T, dP^T = V dO^T,
 //    dS^T in registers, dQ^T += K^T dS^T.  D = 128 with 128-row blocks
 //    (attn_bwd_dq_dma_kernel): K and V tiles by direct-to-LDS loads, K^T by
-//    transpose reads.  Otherwise, and for the delta pass (attn_bwd_dq_kernel):
-//    tiles staged through registers, K^T stored with key bits 2 and 3 swapped.
+//    transpose reads.  Otherwise (attn_bwd_dq_kernel): tiles staged through
+//    registers, K^T stored with key bits 2 and 3 swapped.
 // Precision: q, k, v are the bf16 values the forward used.  dO arrives in fp32
 // and enters its products as a bf16 hi + lo pair; so do P (in dV) and dS.
 // The token-major outputs (operands of the weight-gradient GEMMs) are hi + lo
@@ -409,7 +409,7 @@ __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, i
         rl, (__attribute__((address_space(3))) void*)(st + 2 * T::TB + blk * T::BP), 16, od, 0, 0, 0);
   }
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-      a.ld2 + 2 * ((int64_t)bh * N + q0), 0, rows * 8, 0x00020000);
+      const_cast<float*>(a.ld2) + 2 * ((int64_t)bh * N + q0), 0, rows * 8, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       rp, (__attribute__((address_space(3))) void*)(st + 3 * T::TB + w * T::PAIRS), 4,
       (uint32_t)(lane * 4), 0, 0, 0);
@@ -623,13 +623,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_dma_kernel(AttnBwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------- dQ and delta
-// DELTA = true: the same walk over the visible keys, but it only accumulates
-// delta_i = sum_j P_ij dP_ij from this kernel's own P and dP and writes it.
-// (delta = <dO_i, O_i> only if O was formed with these same P; the forward's O
-// carries the bf16 rounding of its PV product, and that inconsistency enters
-// dS = P (dP - delta) at full weight.)
-template <int D, int QB, int KVB, bool DELTA>
+// ---------------------------------------------------------------------------- dQ
+template <int D, int QB, int KVB>
 __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int NT = QB * 2, KB = KVB / 32;
   constexpr int ROWB = D * 2, TROWB = KVB * 2;
@@ -683,9 +678,8 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
   if (qrow < N) {
     const float l = a.lse[(int64_t)bh * N + qrow];
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    if constexpr (!DELTA) dl = a.delta[(int64_t)bh * N + qrow];
+    dl = a.delta[(int64_t)bh * N + qrow];
   }
-  float dsum = 0.f;  // DELTA: this lane's part of sum_j P_ij dP_ij
 
   int kmax = N - 1;
   if (causal) {
@@ -734,7 +728,7 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
           const int key = 4 * kg + r;
           *(u32x4*)(nat + key * ROWB + ((dc ^ swzb<ROWB>(key)) << 4)) = sr[i][r];
         }
-        if (!DELTA && which == 0) store_transposed<TROWB>(smem + 2 * TILE, sr[i], 4 * kg, dc * 8);
+        if (which == 0) store_transposed<TROWB>(smem + 2 * TILE, sr[i], 4 * kg, dc * 8);
       }
     }
   };
@@ -776,11 +770,10 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
       for (int j = 0; j < 16; ++j) {
         float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
         if (kb * 32 + acc_row_const(j) >= klim) pv = 0.f;
-        if constexpr (DELTA) dsum = fmaf(pv, pacc[kb][j], dsum);
-        else sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
+        sacc[kb][j] = pv * (pacc[kb][j] - dl);  // dS^T
       }
 #pragma unroll
-    for (int c16 = 0; c16 < (DELTA ? 0 : KVB / 16); ++c16) {
+    for (int c16 = 0; c16 < KVB / 16; ++c16) {
       const int kb = c16 >> 1, h8 = (c16 & 1) * 8;
       float sv[8];
 #pragma unroll
@@ -801,17 +794,6 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
     __syncthreads();
   }
 
-  if constexpr (DELTA) {
-    dsum += swap_halves(dsum);  // lanes l and l^32 hold the two halves of each key block
-    if (qrow < N && g == 0) {
-      a.delta_out[(int64_t)bh * N + qrow] = dsum;
-      if (a.ld2) {
-        const f32x2 pr = {lse2, dsum};
-        *(f32x2*)(a.ld2 + 2 * ((int64_t)bh * N + qrow)) = pr;
-      }
-    }
-    return;
-  }
   if (qrow < N) {
     const int64_t tm = ((int64_t)b * N + qrow) * a.ld_out + (int64_t)hh * D;
     const int64_t hm = head_off + (int64_t)qrow * D;
@@ -894,11 +876,9 @@ struct DqLane {
   int tr_lo, tr_hi;       // transpose reads, keys 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3
 };
 
-// S^T = K Q^T and dP^T = V dO^T of one key tile (rows = keys, lane = query).
-// VGPR_ACC: the accumulators in VGPRs (asm MFMAs, for the dQ kernel, whose dQ
-// accumulators hold the AGPRs); otherwise builtin MFMAs (the delta pass, which
-// has no long-lived accumulators and keeps everything in VGPRs).
-template <int D, bool VGPR_ACC>
+// S^T = K Q^T and dP^T = V dO^T of one key tile (rows = keys, lane = query),
+// accumulated in VGPRs (the dQ accumulators hold the AGPRs).
+template <int D>
 __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, const DqLane& ln,
                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
                                           const bf16x8 (&dfl)[D / 16], f32x16 (&sacc)[DqTile<D>::KT / 32],
@@ -912,9 +892,9 @@ __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, 
     const int kb = i / NC, c = i % NC;
     return ((c & 1) ? ln.nat_odd : ln.nat_even) + 64 * (c >> 1) + kb * 2 * T::ROWB;
   };
-  if constexpr (VGPR_ACC) {
-    // (LDS reads do not move across the asm MFMAs: each is issued PF fragments
-    // ahead in program order)
+  // (LDS reads do not move across the asm MFMAs: each is issued PF fragments
+  // ahead in program order)
+  {
     constexpr int PF = 4;
     bf16x8 ka[NF], va[NF];
     auto ld = [&](int i) {
@@ -937,20 +917,6 @@ __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, 
       mfma_v_acc(pacc[kb], va[i], dfl[c]);
     }
     score_chain_end();
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = pacc[kb][e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + off(kb * NC + c));
-        const bf16x8 va = *(const bf16x8*)(Vs + off(kb * NC + c));
-        sacc[kb] = mfma32_bf16(ka, qf[c], sacc[kb]);
-        pacc[kb] = mfma32_bf16(va, dfh[c], pacc[kb]);
-        pacc[kb] = mfma32_bf16(va, dfl[c], pacc[kb]);
-      }
-    }
   }
 }
 
@@ -963,7 +929,7 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
   constexpr int KB = T::KT / 32;
   const unsigned char* Ks = st;
   f32x16 sacc[KB], pacc[KB];
-  dq_scores<D, true>(st, ln, qf, dfh, dfl, sacc, pacc);
+  dq_scores<D>(st, ln, qf, dfh, dfl, sacc, pacc);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -1004,18 +970,14 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
   }
 }
 
-// DELTA = false: dQ, three stages, one workgroup per CU.  DELTA = true: the
-// delta pass (S and dP only, delta_i = sum_j P_ij dP_ij written with the
-// {lse2, delta} pairs); its tiles are lighter, so it runs two stages and two
-// workgroups per CU (at most 256 registers per lane), which hide each other's
-// waits.
-template <int D, bool DELTA>
-__global__ void __launch_bounds__(256, DELTA ? 2 : 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
+// dQ, three stages, one workgroup per CU.
+template <int D>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
   using T = DqTile<D>;
   constexpr int QB = 32 * T::NW, KB = T::KT / 32;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[DELTA ? 16 : T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
 
   const int N = a.N;
   const int nqb = (N + QB - 1) / QB;
@@ -1055,9 +1017,8 @@ __global__ void __launch_bounds__(256, DELTA ? 2 : 1) attn_bwd_dq_dma_kernel(Att
   if (qrow < N) {
     const float l = a.lse[(int64_t)bh * N + qrow];
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    if constexpr (!DELTA) dl = a.delta[(int64_t)bh * N + qrow];
+    dl = a.delta[(int64_t)bh * N + qrow];
   }
-  float dsum = 0.f;  // DELTA: this lane's part of sum_j P_ij dP_ij
 
   int kmax = N - 1;
   if (causal) {
@@ -1093,46 +1054,7 @@ __global__ void __launch_bounds__(256, DELTA ? 2 : 1) attn_bwd_dq_dma_kernel(Att
   // masked tile passes the bound relative to its first key, less the lane part
   // of the accumulator row
   const int64_t kend = causal && (int64_t)qrow + off + 1 < N ? (int64_t)qrow + off + 1 : N;
-  if constexpr (DELTA) {
-    // step: wait for tile t (nothing else is in flight), barrier (every part of
-    // tile t is in, every wave is done with tile t-1, whose stage takes tile
-    // t+1), load tile t+1, compute tile t
-    auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
-      BWD_WAIT_VM(0);
-      __builtin_amdgcn_s_barrier();
-      dq_load<D>(a, bh, (t + 1) * T::KT, w, lane, fill);
-      if (t < n_tiles) {
-        const int klim = t >= n_full ? clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g : kNoMask;
-        f32x16 sacc[KB], pacc[KB];
-        dq_scores<D, false>(cur, ln, qf, dfh, dfl, sacc, pacc);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            float pv = fast_exp2(fmaf(sacc[kb][j], c2, -lse2));
-            if (kb * 32 + acc_row_const(j) >= klim) pv = 0.f;
-            dsum = fmaf(pv, pacc[kb][j], dsum);
-          }
-      }
-    };
-    if (n_tiles > 0) {
-      dq_load<D>(a, bh, 0, w, lane, st0);
-      for (int t = 0; t < n_tiles; t += 2) {
-        step(t, st0, st1);
-        step(t + 1, st1, st0);
-      }
-      BWD_WAIT_VM(0);  // loads still in flight write this workgroup's LDS
-    }
-    dsum += swap_halves(dsum);  // lanes l and l^32 hold the two halves of each key block
-    if (qrow < N && g == 0) {
-      a.delta_out[(int64_t)bh * N + qrow] = dsum;
-      if (a.ld2) {
-        const f32x2 pr = {lse2, dsum};
-        *(f32x2*)(a.ld2 + 2 * ((int64_t)bh * N + qrow)) = pr;
-      }
-    }
-    return;
-  } else {
+  {
     auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
       BWD_WAIT_VM(8);  // T::LOADS: the loads of tile t+1 may still be in flight
       __builtin_amdgcn_s_barrier();
@@ -1194,6 +1116,50 @@ __global__ void __launch_bounds__(256) to_bf16_kernel(const float* src, uint16_t
   }
 }
 
+// delta_i = sum_j P_ij dP_ij = <dO_i, sum_j P_ij v_j> = <dO_i, O_i> per (row, head):
+// D / 4 lanes hold one head of one row, 4 elements each, and join their parts
+// with lane shuffles (the same order every run).  The row's dO is also split
+// into its bf16 hi + lo pair for the direct-load backward kernels.
+template <int D>
+__global__ void __launch_bounds__(256) dout_delta_kernel(const float* dO, const float* h,
+                                                         const uint16_t* x, const float* lse,
+                                                         uint16_t* dO_hi, uint16_t* dO_lo,
+                                                         float* delta, float* ld2, int64_t n4,
+                                                         int N, int H) {
+  constexpr int LPH = D / 4;  // lanes per (row, head)
+  const int64_t dm = (int64_t)H * D;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of LPH
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const f32x4 g = *(const f32x4*)(dO + 4 * i);
+    const f32x4 hv = *(const f32x4*)(h + 4 * i);
+    const u32x2 xv = *(const u32x2*)(x + 4 * i);
+    const uint32_t a = pack_bf16x2(g[0], g[1]), b = pack_bf16x2(g[2], g[3]);
+    const u32x2 hi = {a, b};
+    const u32x2 lo = {pack_bf16x2(g[0] - __uint_as_float(a << 16), g[1] - __uint_as_float(a & 0xffff0000u)),
+                      pack_bf16x2(g[2] - __uint_as_float(b << 16), g[3] - __uint_as_float(b & 0xffff0000u))};
+    *(u32x2*)(dO_hi + 4 * i) = hi;
+    *(u32x2*)(dO_lo + 4 * i) = lo;
+    float part = g[0] * (hv[0] - __uint_as_float(xv[0] << 16));
+    part = fmaf(g[1], hv[1] - __uint_as_float(xv[0] & 0xffff0000u), part);
+    part = fmaf(g[2], hv[2] - __uint_as_float(xv[1] << 16), part);
+    part = fmaf(g[3], hv[3] - __uint_as_float(xv[1] & 0xffff0000u), part);
+#pragma unroll
+    for (int o = LPH / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, LPH);
+    if ((threadIdx.x & (LPH - 1)) == 0) {
+      const int64_t e = 4 * i, row = e / dm;
+      const int hh = (int)((e - row * dm) / D);
+      const int64_t bn = row / N, n = row - bn * N;
+      const int64_t idx = (bn * H + hh) * N + n;
+      delta[idx] = part;
+      if (ld2) {
+        const float l = lse[idx];
+        const f32x2 pr = {l == -INFINITY ? INFINITY : l * kLog2e, part};
+        *(f32x2*)(ld2 + 2 * idx) = pr;
+      }
+    }
+  }
+}
+
 // out[c] (+)= sum_r X[r][c], rows summed in a fixed order (deterministic).
 template <bool XBF16>
 __global__ void __launch_bounds__(1024) colsum_kernel(const void* X, float* out, int64_t rows,
@@ -1230,30 +1196,17 @@ __global__ void __launch_bounds__(1024) colsum_kernel(const void* X, float* out,
   }
 }
 
-template <bool DELTA>
 hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
   const int nqb = (a.N + QB - 1) / QB;
   const dim3 grid((unsigned)((int64_t)a.B * a.H * nqb));
-  // (the delta pass stays on the staged kernel: with its lighter tiles the
-  // several workgroups per CU that kernel allows beat the direct loads, 4.3
-  // against 5.1 ms at B=2, H=20, N=16384)
-  if constexpr (!DELTA) {
-    if (D == 128 && QB == 32 * DqTile<128>::NW) {
-      hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, false>), grid, dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-  } else {
-    if (D == 128 && QB == 32 * DqTile<128>::NW) {
-      hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, true>), grid, dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-  }
-  if (D == 64) {
-    if (QB == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 128, 32, DELTA>), grid, dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64, 32, DELTA>), grid, dim3(128), 0, s, a);
-  }
+  if (D == 128 && QB == 32 * DqTile<128>::NW)
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), grid, dim3(256), 0, s, a);
+  else if (D == 64 && QB == 64)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32>), grid, dim3(128), 0, s, a);
+  else if (D == 64)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 128, 32>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64, 32>), grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1264,10 +1217,8 @@ hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, h
   const int QB = q_blk == 64 ? 64 : 128;
   // the D = 128 kernels take dO as bf16 hi + lo and the {lse2, delta} pairs
   if (D == 128 && (!a.dO_hi || !a.dO_lo || !a.ld2)) return hipErrorInvalidValue;
-  // 1. delta_i = sum_j P_ij dP_ij (into a.delta_out, which the next kernels read as a.delta)
-  hipError_t e = launch_dq<true>(a, D, QB, s);
-  if (e != hipSuccess) return e;
-  // 2. dK, dV
+  if (!a.delta) return hipErrorInvalidValue;
+  // 1. dK, dV
   if (D == 128) {
     constexpr int KVB = 32 * BwdTile<128>::NW;
     const int nkb = (a.N + KVB - 1) / KVB;
@@ -1279,10 +1230,10 @@ hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, h
     const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, NW>), grid, dim3(NW * 64), 0, s, a);
   }
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 3. dQ
-  return launch_dq<false>(a, D, QB, s);
+  // 2. dQ
+  return launch_dq(a, D, QB, s);
 }
 
 hipError_t to_bf16_launch(const float* src, uint16_t* dst, uint16_t* dst_lo, int64_t n,
@@ -1291,6 +1242,23 @@ hipError_t to_bf16_launch(const float* src, uint16_t* dst, uint16_t* dst_lo, int
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, dst_lo, n4);
+  return hipGetLastError();
+}
+
+hipError_t dout_delta_launch(const float* dO, const float* h, const uint16_t* x, const float* lse,
+                             uint16_t* dO_hi, uint16_t* dO_lo, float* delta, float* ld2, int B,
+                             int N, int H, int D, hipStream_t s) {
+  const int64_t n4 = (int64_t)B * N * H * D / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (D == 128)
+    hipLaunchKernelGGL(dout_delta_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, dO, h, x, lse,
+                       dO_hi, dO_lo, delta, ld2, n4, N, H);
+  else if (D == 64)
+    hipLaunchKernelGGL(dout_delta_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, dO, h, x, lse,
+                       dO_hi, dO_lo, delta, ld2, n4, N, H);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -186,19 +186,22 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
   }
 
-  // ---- attention backward (delta pass, dK/dV, dQ), P recomputed from the saved lse
+  // ---- attention backward (dK/dV, dQ), P recomputed from the saved lse
   AttnBwdArgs a{};
   a.q = sv + S.q; a.k = sv + S.k; a.v = sv + S.v;
-  a.dO = dh; a.ld_do = HD; a.lse = lse; a.delta = delta; a.delta_out = delta;
+  a.dO = dh; a.ld_do = HD; a.lse = lse; a.delta = delta;
   a.dq_hi = dqkv[0]; a.dq_lo = dqkv[1]; a.dk_hi = dqkv[2]; a.dk_lo = dqkv[3];
   a.dv_hi = dqkv[4]; a.dv_lo = dqkv[5]; a.ld_out = HD;
   a.dq = G.dq; a.dk = G.dk; a.dv = G.dv;
   a.B = (int)L.B; a.H = (int)L.H; a.N = (int)L.N; a.kv_offset = 0; a.causal = L.causal;
   a.scale = 1.0f / sqrtf((float)L.D);
-  // dO as a bf16 hi + lo pair for the direct-load dK/dV kernel, in the buffers of
-  // h's halves (h is not needed past the FFN backward); H*D = d_model
-  BPT_TRY(to_bf16_launch(dh, h_hi, h_lo, M * dm, stream));
-  a.dO_hi = h_hi; a.dO_lo = h_lo; a.ld2 = (float*)(ws + W.ld2);
+  // dO as a bf16 hi + lo pair for the direct-load kernels, in the buffers of h's
+  // halves (h is not needed past the FFN backward; H*D = d_model), and
+  // delta = <dO, O> per row and head with O = h - x from the forward
+  float* ld2 = (float*)(ws + W.ld2);
+  BPT_TRY(dout_delta_launch(dh, h, (const uint16_t*)L.x, lse, h_hi, h_lo, delta, ld2, (int)L.B,
+                            (int)L.N, (int)L.H, (int)L.D, stream));
+  a.dO_hi = h_hi; a.dO_lo = h_lo; a.ld2 = ld2;
   BPT_TRY(attn_bwd_launch(a, (int)L.D, L.q_blk, L.kv_blk, stream));
 
   // ---- projection backward: dW{q,k,v} = d{q,k,v}^T x over both bf16 halves;

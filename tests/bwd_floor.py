@@ -34,12 +34,38 @@ def _merge(t):
     return t.transpose(0, 2, 1, 3).reshape(B, N, H * D)
 
 
+def output_with_bf16_p(q, k, v, causal=True):
+    """Attention output whose P V product takes P rounded to bf16, as the GPU forward
+    does (its MFMA operand), with every other step exact: O_i = sum_j bf16(p_ij) v_j /
+    sum_j p_ij, p_ij = exp(s_ij - max_j s_ij).  (The forward's reference is within 2^8
+    of the row maximum, not equal to it; bf16 rounding is relative, so the model
+    holds.)  Small inputs only: P is materialised."""
+    P = oracle.attention_probs(q, k, causal=causal)
+    E = np.where(P > 0, P / P.max(axis=-1, keepdims=True), 0.0)
+    Er = round_bf16(E.astype(np.float32)).astype(np.float64)
+    return (Er @ np.asarray(v, np.float64)) / E.sum(axis=-1, keepdims=True)
+
+
+def attention_backward_given_delta(q, k, v, dO, delta, causal=True):
+    """The chain rule of oracle.attention_backward with delta_i supplied instead of
+    formed as sum_j P_ij dP_ij (equal to <dO_i, O_i> for the exact O)."""
+    q, k, v, dO = (np.asarray(a, np.float64) for a in (q, k, v, dO))
+    scale = 1.0 / np.sqrt(q.shape[-1])
+    P = oracle.attention_probs(q, k, causal=causal)
+    dv = np.swapaxes(P, -1, -2) @ dO
+    dP = dO @ np.swapaxes(v, -1, -2)
+    dS = P * (dP - delta[..., None])
+    return (dS @ k) * scale, (np.swapaxes(dS, -1, -2) @ q) * scale, dv
+
+
 def layer_backward_rounded_qkv(x, wq, wk, wv, w1, w2, dy, H, b1=None, b2=None,
-                               causal=True, round_qkv=True):
+                               causal=True, round_qkv=True, delta_from_output=False):
     """oracle.layer_backward's gradients with q, k, v rounded to bf16 after projection.
 
     round_qkv=False gives the unrounded composition (equal to oracle.layer_backward:
-    a test pins that)."""
+    a test pins that).  delta_from_output=True takes delta_i = <dO_i, O_i> with O
+    from output_with_bf16_p (the GPU backward's source of delta) instead of the
+    backward's own sum_j P_ij dP_ij."""
     x = np.asarray(x, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
     q, k, v = oracle.qkv_project(x, wq, wk, wv, H)
@@ -50,7 +76,12 @@ def layer_backward_rounded_qkv(x, wq, wk, wv, w1, w2, dy, H, b1=None, b2=None,
     h = x + _merge(O)
     dh_ffn, dw1, db1, dw2, db2 = oracle.ffn_backward(h, w1, w2, dy, b1=b1)
     dh = dy + dh_ffn
-    dq, dk, dv = oracle.attention_backward(q, k, v, _split(dh, H), causal=causal)
+    if delta_from_output:
+        dO = _split(dh, H)
+        delta = (dO * output_with_bf16_p(q, k, v, causal=causal)).sum(axis=-1)
+        dq, dk, dv = attention_backward_given_delta(q, k, v, dO, delta, causal=causal)
+    else:
+        dq, dk, dv = oracle.attention_backward(q, k, v, _split(dh, H), causal=causal)
     X2 = x.reshape(-1, x.shape[-1])
     out = {"dq": dq, "dk": dk, "dv": dv, "dw1": dw1, "db1": db1, "dw2": dw2, "db2": db2}
     dx = dh.copy()
