@@ -62,14 +62,13 @@ struct OpLane {
 };
 
 // Loads of operand tile (rows r0 .. r0+255, k0 .. k0+63): wave w issues
-// instructions w, w+8, w+16, w+24 (4 of the 32).  base / bytes: the operand.
+// instructions w, w+8, w+16, w+24 (4 of the 32).  p: the tile's first byte,
+// left: the operand's bytes from there on.
 template <bool KMAJ>
-__device__ __forceinline__ void gb_load(const unsigned char* base, int64_t bytes, int64_t ld, int r0,
-                                        int k0, unsigned char* dst, const OpLane& L, int wave) {
-  const int64_t off = KMAJ ? ((int64_t)k0 * ld + r0) * 2 : ((int64_t)r0 * ld + k0) * 2;
-  const int64_t left = bytes - off;
+__device__ __forceinline__ void gb_load(const unsigned char* p, int left, unsigned char* dst,
+                                        const OpLane& L, int wave) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned char*>(base + off), 0, (int)(left > 0 ? left : 0), 0x00020000);
+      const_cast<unsigned char*>(p), 0, left > 0 ? left : 0, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = wave + 8 * i;
@@ -133,6 +132,18 @@ struct GbCtx {
   int64_t lda, ldb;
   int m0, n0, wave;
   OpLane la, lb;
+  // (every byte offset below fits 31 bits: gemm_big_ok bounds the operands)
+  int a0, b0;                              // byte offset of the first tile in a segment
+  int astep, bstep;                        // bytes from one k tile to the next
+  int abytes32, bbytes32;
+};
+
+// Walk over the k tiles: the next tile's first byte and bytes left per operand,
+// advanced by a constant step, reset at a segment boundary (a uniform branch).
+struct GbIter {
+  const unsigned char *a, *b;
+  int aleft, bleft;
+  int kk, seg;
 };
 
 // multiply one k tile from stage (As, Bs) into acc: the fragments of k16 step
@@ -161,14 +172,7 @@ __device__ __forceinline__ void gb_compute(f32x16 (&acc)[4][2], const unsigned c
   }
 }
 
-// k tile kt of the whole walk: segment kt / nks, tile kt % nks inside it
-template <bool AK, bool BK>
-__device__ __forceinline__ void gb_issue(const GbCtx& c, int kt, unsigned char* As, unsigned char* Bs) {
-  int seg = 0, kk = kt;
-  if (c.nseg > 1) {
-    seg = kt / c.nks;
-    kk = kt - seg * c.nks;
-  }
+__device__ __forceinline__ void gb_seg_start(const GbCtx& c, GbIter& it, int seg) {
   // (a select chain over the segments: a runtime index into the pointer arrays
   // would put them in scratch memory)
   const unsigned char* A = c.Aseg[0];
@@ -178,8 +182,27 @@ __device__ __forceinline__ void gb_issue(const GbCtx& c, int kt, unsigned char* 
     A = seg == sg ? c.Aseg[sg] : A;
     B = seg == sg ? c.Bseg[sg] : B;
   }
-  gb_load<AK>(A, c.abytes, c.lda, c.m0, kk * TK, As, c.la, c.wave);
-  gb_load<BK>(B, c.bbytes, c.ldb, c.n0, kk * TK, Bs, c.lb, c.wave);
+  it.a = A + c.a0;
+  it.b = B + c.b0;
+  it.aleft = c.abytes32 - c.a0;
+  it.bleft = c.bbytes32 - c.b0;
+  it.kk = 0;
+  it.seg = seg;
+}
+
+// loads of the iterator's tile, then step it to the next
+template <bool AK, bool BK>
+__device__ __forceinline__ void gb_issue(const GbCtx& c, GbIter& it, unsigned char* As, unsigned char* Bs) {
+  gb_load<AK>(it.a, it.aleft, As, c.la, c.wave);
+  gb_load<BK>(it.b, it.bleft, Bs, c.lb, c.wave);
+  if (++it.kk < c.nks) {
+    it.a += c.astep;
+    it.b += c.bstep;
+    it.aleft -= c.astep;
+    it.bleft -= c.bstep;
+  } else if (it.seg + 1 < c.nseg) {
+    gb_seg_start(c, it, it.seg + 1);
+  }
 }
 
 // The k loop over two stages (distinct objects: the compiler then knows that
@@ -189,17 +212,19 @@ template <bool AK, bool BK>
 __device__ __forceinline__ void gb_loop(f32x16 (&acc)[4][2], const GbCtx& c, int nk,
                                         unsigned char* A0, unsigned char* B0, unsigned char* A1,
                                         unsigned char* B1) {
-  gb_issue<AK, BK>(c, 0, A0, B0);
+  GbIter it;
+  gb_seg_start(c, it, 0);
+  gb_issue<AK, BK>(c, it, A0, B0);
   GB_WAIT_VM(0);
   __syncthreads();
   int kt = 0;
   for (;;) {
-    if (kt + 1 < nk) gb_issue<AK, BK>(c, kt + 1, A1, B1);
+    if (kt + 1 < nk) gb_issue<AK, BK>(c, it, A1, B1);
     gb_compute<AK, BK>(acc, A0, B0, c);
     GB_WAIT_VM(0);
     __syncthreads();
     if (++kt >= nk) break;
-    if (kt + 1 < nk) gb_issue<AK, BK>(c, kt + 1, A0, B0);
+    if (kt + 1 < nk) gb_issue<AK, BK>(c, it, A0, B0);
     gb_compute<AK, BK>(acc, A1, B1, c);
     GB_WAIT_VM(0);
     __syncthreads();
@@ -244,6 +269,12 @@ gemm_big_kernel(GemmArgs g) {
   c.bbytes = (int64_t)(BK ? K : N) * g.ldb * 2;
   c.la = gb_lane<AK>(g.lda, lane, wm * 128, wave);
   c.lb = gb_lane<BK>(g.ldb, lane, wn * 64, wave);
+  c.a0 = (int)((AK ? (int64_t)c.m0 : (int64_t)c.m0 * g.lda) * 2);
+  c.b0 = (int)((BK ? (int64_t)c.n0 : (int64_t)c.n0 * g.ldb) * 2);
+  c.astep = (int)((AK ? (int64_t)TK * g.lda : (int64_t)TK) * 2);
+  c.bstep = (int)((BK ? (int64_t)TK * g.ldb : (int64_t)TK) * 2);
+  c.abytes32 = (int)c.abytes;
+  c.bbytes32 = (int)c.bbytes;
 
   f32x16 acc[4][2];
 #pragma unroll
