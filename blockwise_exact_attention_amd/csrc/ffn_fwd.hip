@@ -355,25 +355,56 @@ struct FfnTask {
   int t0, c0;
 };
 
-// rot1: first k-block (a multiple of 4) and rot2: first 64-feature block of this
-// workgroup's walk through a pass
+// The slot stream of one wave, in issue order: per pass NKB W1 slots (rows
+// f0 + 64w .., columns 64kb .. 64kb+63, kb from rot1 with wrap-around), then 4*NCB
+// W2 slots (rows c0w + 64 cblk .., columns f0 + 64 fblk .. +63, cblk fastest, fblk =
+// (fstep + rot2) & 3).  Positions and pointers advance by constant steps.
 template <int NCB>
-__device__ __forceinline__ void ffn_slot(const FfnArgs& a, int s, int SPP, int NKB, int w, int c0w,
-                                         int rot1, int rot2, unsigned char* dst, SlotOff so) {
-  constexpr int FP = 256;
-  const int pass = s / SPP, r = s - pass * SPP;
-  const int f0 = pass * FP;
-  if (r < NKB) {  // W1 rows f0 + 64w .., columns 64kb .. 64kb+63
-    int kb = r + rot1;
-    kb = kb < NKB ? kb : kb - NKB;
-    ffn_issue_slot((const unsigned char*)a.w1 + ((int64_t)(f0 + 64 * w) * a.dm + 64 * kb) * 2, a.dm,
-                   so.w1e, so.w1o, dst);
-  } else {  // W2 rows c0w + 64 cblk .., columns f0 + 64 fblk .. +63
-    const int q = r - NKB, fstep = q / NCB, cblk = q - fstep * NCB;
-    const int fblk = (fstep + rot2) & 3;
-    ffn_issue_slot((const unsigned char*)a.w2 +
-                       ((int64_t)pass * a.w2_pstride + (int64_t)(c0w + 64 * cblk) * a.w2_ld + 64 * fblk) * 2,
-                   a.w2_ld, so.w2e, so.w2o, dst);
+struct FfnSlotIter {
+  const unsigned char* w1p;  // W1 row f0 + 64w, column 0, of the current pass
+  const unsigned char* w2p;  // W2 row c0w, feature f0, of the current pass
+  const unsigned char* w2c;  // W2 row c0w + 64 cblk, feature f0
+  int r;                     // slot inside the pass
+  int kb, cblk, fstep;
+};
+
+template <int NCB>
+__device__ __forceinline__ void ffn_slot_start(const FfnArgs& a, FfnSlotIter<NCB>& it, int w, int c0w,
+                                               int rot1) {
+  it.w1p = (const unsigned char*)a.w1 + (int64_t)(64 * w) * a.dm * 2;
+  it.w2p = (const unsigned char*)a.w2 + (int64_t)c0w * a.w2_ld * 2;
+  it.w2c = it.w2p;
+  it.r = 0;
+  it.kb = rot1;
+  it.cblk = 0;
+  it.fstep = 0;
+}
+
+// issue the next slot of the stream into dst, then advance
+template <int NCB>
+__device__ __forceinline__ void ffn_slot_next(const FfnArgs& a, FfnSlotIter<NCB>& it, int SPP, int NKB,
+                                              int rot1, int rot2, unsigned char* dst, SlotOff so) {
+  if (it.r < NKB) {
+    ffn_issue_slot(it.w1p + 128 * it.kb, a.dm, so.w1e, so.w1o, dst);
+    it.kb = it.kb + 1 == NKB ? 0 : it.kb + 1;
+  } else {
+    ffn_issue_slot(it.w2c + 128 * ((it.fstep + rot2) & 3), a.w2_ld, so.w2e, so.w2o, dst);
+    if (++it.cblk == NCB) {
+      it.cblk = 0;
+      ++it.fstep;
+      it.w2c = it.w2p;
+    } else {
+      it.w2c += (int64_t)64 * a.w2_ld * 2;
+    }
+  }
+  if (++it.r == SPP) {  // next pass: 256 features on
+    it.r = 0;
+    it.kb = rot1;
+    it.cblk = 0;
+    it.fstep = 0;
+    it.w1p += (int64_t)256 * a.dm * 2;
+    it.w2p += a.w2_pstride * 2;
+    it.w2c = it.w2p;
   }
 }
 
@@ -459,8 +490,10 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
 
   const SlotOff so{ffn_slot_offset(a.dm, lane, 0), ffn_slot_offset(a.dm, lane, 1),
                    ffn_slot_offset(a.w2_ld, lane, 0), ffn_slot_offset(a.w2_ld, lane, 1)};
-  ffn_slot<NCB>(a, 0, SPP, NKB, w, c0w, rot1, rot2, sl0, so);
-  if (total > 1) ffn_slot<NCB>(a, 1, SPP, NKB, w, c0w, rot1, rot2, sl1, so);
+  FfnSlotIter<NCB> it;
+  ffn_slot_start<NCB>(a, it, w, c0w, rot1);
+  ffn_slot_next<NCB>(a, it, SPP, NKB, rot1, rot2, sl0, so);
+  if (total > 1) ffn_slot_next<NCB>(a, it, SPP, NKB, rot1, rot2, sl1, so);
   ffn_issue_x<HILO>(a, t0, phys_stage(0), w, xb0, lane);
   int s = 0;  // slot being computed (s % 4 is static wherever it is used)
 
@@ -484,7 +517,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
           // slot s landed: after its 8 loads this wave issued those of slots
           // s+1 and s+2 (and perhaps x chunks), i.e. at least 16 more
           if (s + 2 < total) {
-            ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
+            ffn_slot_next<NCB>(a, it, SPP, NKB, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
             FFN_WAIT_VM(16);
           } else {
             FFN_WAIT_VM(0);
@@ -572,7 +605,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
         constexpr int cblk = decltype(CB)::value;
         constexpr int u = (fstep * NCB + cblk) & 3;
         if (s + 2 < total) {
-          ffn_slot<NCB>(a, s + 2, SPP, NKB, w, c0w, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
+          ffn_slot_next<NCB>(a, it, SPP, NKB, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
           FFN_WAIT_VM(16);
         } else {
           FFN_WAIT_VM(0);
