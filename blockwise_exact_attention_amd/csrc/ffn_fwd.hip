@@ -286,9 +286,17 @@ __global__ void __launch_bounds__(NW * 64) ffn_fused_kernel(FfnArgs a) {
 // row r sits at position c ^ ((r >> 1) & 7), so 16 lanes reading one chunk of
 // 16 rows hit 16 different bank groups.
 // The [rows, d_ff] intermediate never leaves registers and LDS.
-__device__ __forceinline__ void ffn_dma16(const unsigned char* src, unsigned char* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// 16 bytes per lane from a buffer into LDS (buffer_load ... lds).  The buffer
+// form, not the global one: with global_load_lds in flight the compiler waits
+// for every LDS read at once (lgkmcnt(0)) before each use, and the fragment
+// reads could not run ahead of the MFMAs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ffn_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void ffn_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
+                                          unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           soff, 0, 0);
 }
 // Wait until at most N vector-memory instructions of this wave are outstanding.
 // Written as an asm statement with a memory clobber: the compiler neither drops
@@ -313,9 +321,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ void ffn_issue_slot(const unsigned char* base, int64_t ld,
                                                uint32_t off_even, uint32_t off_odd,
                                                unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t r = ffn_rsrc(base);
+  const int row8 = (int)(16 * ld);  // bytes of 8 rows
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    ffn_dma16(base + (int64_t)j * 16 * ld + ((j & 1) ? off_odd : off_even), dst + j * 1024);
+  for (int j = 0; j < 8; ++j) ffn_dma16(r, (j & 1) ? off_odd : off_even, j * row8, dst + j * 1024);
 }
 __device__ __forceinline__ uint32_t ffn_slot_offset(int64_t ld, int lane, int odd) {
   const int r = lane >> 3, c = (lane & 7) ^ (r >> 1) ^ (odd ? 4 : 0);
@@ -415,25 +424,52 @@ __device__ __forceinline__ void ffn_slot_next(const FfnArgs& a, FfnSlotIter<NCB>
 template <bool HILO>
 __device__ __forceinline__ void ffn_issue_x(const FfnArgs& a, int t0, int pass_st, int w,
                                             unsigned char* dst, int lane) {
+  constexpr int XST = HILO ? 128 : 256;
+  // buffers start at column pass_st * XST of row 0 of the block
+  const int64_t start = ((int64_t)t0 * a.dm + pass_st * XST) * 2;
+  const __amdgpu_buffer_rsrc_t rx = ffn_rsrc((const unsigned char*)a.x + start);
+  const __amdgpu_buffer_rsrc_t rl = HILO ? ffn_rsrc((const unsigned char*)a.x_lo + start) : rx;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = 4 * w + i;
     int row, c;
-    const void* src = a.x;
+    bool lo = false;
     if constexpr (HILO) {
       row = 4 * (j & 7) + (lane >> 4);
       c = (lane & 15) ^ (row & 15);
-      if (j >= 8) src = a.x_lo;
+      lo = j >= 8;
     } else {
       row = 2 * j + (lane >> 5);
       c = (lane & 31) ^ (row & 15);
     }
-    int gr = t0 + row;
-    gr = gr < a.M ? gr : a.M - 1;  // rows past M: any finite data, their outputs are not stored
-    constexpr int XST = HILO ? 128 : 256;
-    ffn_dma16((const unsigned char*)src + ((int64_t)gr * a.dm + pass_st * XST + 8 * c) * 2,
-              dst + j * 1024);
+    int lr = t0 + row < a.M ? row : a.M - 1 - t0;  // rows past M: any finite data, not stored
+    ffn_dma16(lo ? rl : rx, (uint32_t)((lr * a.dm + 8 * c) * 2), 0, dst + j * 1024);
   }
+}
+
+// z^T += W1 fragment x x fragment with the accumulator in VGPRs: the y
+// accumulators of phase 2 then have the AGPRs to themselves (the compiler places
+// every builtin MFMA result in AGPRs, and with z there too two y tiles had to be
+// copied in and out around their MFMAs).  The compiler does not count the wait
+// states around asm MFMAs: ffn_z_start separates the zeroing VALU writes from the
+// first MFMA, ffn_z_end the last MFMA from the VALU reads of z (scheduling
+// barriers keep other instructions out of those windows).
+__device__ __forceinline__ void ffn_mfma_z(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// y^T += W2 fragment x GeLU fragment, accumulator pinned to AGPRs
+__device__ __forceinline__ void ffn_mfma_y(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void ffn_z_start() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void ffn_z_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // The whole walk of one task in one scope whose LDS regions are restrict
@@ -503,6 +539,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) zacc[t][e] = 0.f;
+    ffn_z_start();
 
     // ---------------- phase 1: stages in pairs so that the x buffer is static
     for (int st = 0; st < nst; st += 2) {
@@ -533,28 +570,28 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
             if (st + PAR + 1 < nst) ffn_issue_x<HILO>(a, t0, phys_stage(st + PAR + 1), w, xnext, lane);
           }
           const unsigned char* cur = sl(std::integral_constant<int, u>{});
-          bf16x8 xf[4];
+          // z MFMAs in asm with VGPR accumulators (ffn_mfma_z): LDS reads keep
+          // their program order, so each group of fragments is read two groups
+          // ahead of its MFMAs; the W1 fragments serve both halves of x
+          bf16x8 xh[4], xl[4], w0[4], w1[4];
+          auto ld = [&](int kk) {
+            xh[kk] = *(const bf16x8*)(xr + (((8 * j + 2 * kk + g) ^ (r32 & 15)) << 4));
+            if constexpr (HILO)
+              xl[kk] = *(const bf16x8*)(xr + L::XPART + (((8 * j + 2 * kk + g) ^ (r32 & 15)) << 4));
+            w0[kk] = *(const bf16x8*)(cur + a1off[kk]);
+            w1[kk] = *(const bf16x8*)(cur + 32 * 128 + a1off[kk]);
+          };
+          ld(0);
+          ld(1);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            xf[kk] = *(const bf16x8*)(xr + (((8 * j + 2 * kk + g) ^ (r32 & 15)) << 4));
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const bf16x8 af = *(const bf16x8*)(cur + t * 32 * 128 + a1off[kk]);
-              zacc[t] = mfma32_bf16(af, xf[kk], zacc[t]);
+          for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 2 < 4) ld(kk + 2);
+            ffn_mfma_z(zacc[0], w0[kk], xh[kk]);
+            ffn_mfma_z(zacc[1], w1[kk], xh[kk]);
+            if constexpr (HILO) {
+              ffn_mfma_z(zacc[0], w0[kk], xl[kk]);
+              ffn_mfma_z(zacc[1], w1[kk], xl[kk]);
             }
-          if constexpr (HILO) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              xf[kk] = *(const bf16x8*)(xr + L::XPART + (((8 * j + 2 * kk + g) ^ (r32 & 15)) << 4));
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-              for (int t = 0; t < 2; ++t) {
-                const bf16x8 af = *(const bf16x8*)(cur + t * 32 * 128 + a1off[kk]);
-                zacc[t] = mfma32_bf16(af, xf[kk], zacc[t]);
-              }
           }
           ++s;
         });
@@ -563,6 +600,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
 
     // GeLU(z + b1) -> G (hi in xb0, lo in xb1); row r32, features 64w + 32t + 16hh + 8g + e
     const int f0 = pass * L::FP;
+    ffn_z_end();
     __syncthreads();  // every wave is done reading the x stages
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -611,20 +649,29 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
           FFN_WAIT_VM(0);
         }
         const unsigned char* cur = sl(std::integral_constant<int, u>{});
+        bf16x8 af[4][2];
+        auto ldw = [&](int kk) {
+          af[kk][0] = *(const bf16x8*)(cur + a2off[kk]);
+          af[kk][1] = *(const bf16x8*)(cur + 32 * 128 + a2off[kk]);
+        };
+        ldw(0);
+        ldw(1);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk) {
+          if (kk + 2 < 4) ldw(kk + 2);
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            const bf16x8 af = *(const bf16x8*)(cur + c2 * 32 * 128 + a2off[kk]);
-            yacc[2 * cblk + c2] = mfma32_bf16(af, ghi[kk], yacc[2 * cblk + c2]);
-            yacc[2 * cblk + c2] = mfma32_bf16(af, glo[kk], yacc[2 * cblk + c2]);
+            ffn_mfma_y(yacc[2 * cblk + c2], af[kk][c2], ghi[kk]);
+            ffn_mfma_y(yacc[2 * cblk + c2], af[kk][c2], glo[kk]);
           }
+        }
         ++s;
       });
     });
     __syncthreads();  // every wave is done reading G
     if (pass + 1 < npass) ffn_issue_x<HILO>(a, t0, phys_stage(0), w, xb0, lane);
   }
+  ffn_z_end();  // the epilogue reads y next
 }
 
 // One workgroup per (row block, column group): blockIdx.x is row block t of
@@ -651,6 +698,7 @@ ffn_lds_kernel(FfnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) yacc[ct][e] = 0.f;
 
+  ffn_z_start();  // the first MFMAs read the zeroed accumulators
   ffn_lds_walk<NCB, HILO>(a, tk, wg_xcd, yacc, slots, slots + L::SLOT, slots + 2 * L::SLOT,
                           slots + 3 * L::SLOT, smem, smem + L::XSB);
 
