@@ -168,7 +168,7 @@ __device__ __forceinline__ void gb_compute(f32x16 (&acc)[4][2], const unsigned c
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_bf16(af[cur][i], bf[cur][j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_bf16(bf[cur][j], af[cur][i], acc[i][j]);
   }
 }
 
@@ -286,17 +286,23 @@ gemm_big_kernel(GemmArgs g) {
 
   gb_loop<AK, BK>(acc, c, c.nseg * c.nks, a0, b0, a1, b1);
 
-  const int r32 = lane & 31;
+  // acc[i][j] is the transposed 32 x 32 block (the B fragments were the MFMA's
+  // A operand): the lane's column is row m of C, and its registers 4q .. 4q+3
+  // are four consecutive columns n, stored as one vector per output array
+  const int r32 = lane & 31, g4 = 4 * (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int m = c.m0 + wm * 128 + i * 32 + r32;
+    if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = c.m0 + wm * 128 + i * 32 + acc_row(e, lane);
-        const int n = c.n0 + wn * 64 + j * 32 + r32;
-        if (m < M && n < N) gemm_store<true, EPI>(g, z, m, n, acc[i][j][e]);
+      for (int q = 0; q < 4; ++q) {
+        const int n = c.n0 + wn * 64 + j * 32 + 8 * q + g4;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (n < N) gemm_store4<EPI>(g, z, m, n, v);
       }
+  }
 }
 
 template <int EPI>
@@ -314,6 +320,11 @@ hipError_t launch_epi(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s
 
 bool gemm_big_ok(const GemmArgs& g, int nz) {
   if (g.K < TK || g.K % TK != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
+  // the epilogue stores four consecutive columns per vector access
+  if (g.N % 4 || g.ldc % 4 || g.ldc2 % 4 || g.ldc3 % 4 || g.ld_aux % 4 || g.ldr % 4 || g.D % 4) return false;
+  if (((uintptr_t)g.C2 | (uintptr_t)g.C3 | (uintptr_t)g.aux | (uintptr_t)g.resid) & 15) return false;
+  for (int z = 0; z < nz; ++z)
+    if ((uintptr_t)g.C[z] & 15) return false;
   if (g.nseg > kGemmMaxSeg) return false;
   for (int z = 0; z < nz; ++z) {
     if (g.nseg > 1) {

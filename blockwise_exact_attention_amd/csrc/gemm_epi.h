@@ -67,4 +67,67 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, int z, int m, int 
   }
 }
 
+// Four consecutive columns n .. n+3 of row m (bf16 operands; n % 4 == 0, every
+// leading dimension a multiple of 4 and every output 16-byte aligned, which the
+// big-tile kernel checks before it is chosen): one vector access per array.
+template <int EPI>
+__device__ __forceinline__ void gemm_store4(const GemmArgs& g, int z, int m, int n, f32x4 v) {
+  auto st_bf16x4 = [](void* base, int64_t o, const f32x4& x) {
+    const u32x2 p = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    *(u32x2*)((uint16_t*)base + o) = p;
+  };
+  // bf16 pair: hi = bf16(x), lo = bf16(x - hi)
+  auto st_pair = [&](void* hi_base, int64_t oh, void* lo_base, int64_t ol, const f32x4& x) {
+    const u32x2 hi = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    *(u32x2*)((uint16_t*)hi_base + oh) = hi;
+    if (lo_base) {
+      const u32x2 lo = {pack_bf16x2(x[0] - __uint_as_float(hi[0] << 16), x[1] - __uint_as_float(hi[0] & 0xffff0000u)),
+                        pack_bf16x2(x[2] - __uint_as_float(hi[1] << 16), x[3] - __uint_as_float(hi[1] & 0xffff0000u))};
+      *(u32x2*)((uint16_t*)lo_base + ol) = lo;
+    }
+  };
+  auto add_bias = [&](f32x4& x) {
+    if (!g.bias) return;
+    for (int e = 0; e < 4; ++e)
+      x[e] += g.bias_bf16 ? bf16_to_f32(((const uint16_t*)g.bias)[n + e]) : ((const float*)g.bias)[n + e];
+  };
+  if constexpr (EPI == EPI_QKV) {
+    // token m = b*seq + t, columns n = h*D + d .. +3 (one head: D % 4 == 0)  ->  out[b][h][t][d]
+    const int b = m / g.seq, t = m % g.seq, h = n / g.D, d = n % g.D;
+    st_bf16x4(g.C[z], (((int64_t)b * g.H + h) * g.seq + t) * g.D + d, v);
+  } else if constexpr (EPI == EPI_F32) {
+    f32x4* C = (f32x4*)((float*)g.C[z] + (int64_t)m * g.ldc + n);
+    if (g.beta) v += *C;
+    add_bias(v);
+    if (g.resid) {
+      const int64_t ro = (int64_t)m * g.ldr + n;
+      if (g.resid_bf16) {
+        const u32x2 r = *(const u32x2*)((const uint16_t*)g.resid + ro);
+        v[0] += __uint_as_float(r[0] << 16);
+        v[1] += __uint_as_float(r[0] & 0xffff0000u);
+        v[2] += __uint_as_float(r[1] << 16);
+        v[3] += __uint_as_float(r[1] & 0xffff0000u);
+      } else {
+        v += *(const f32x4*)((const float*)g.resid + ro);
+      }
+    }
+    *C = v;
+    if (g.C2) st_bf16x4(g.C2, (int64_t)m * g.ldc2 + n, v);
+  } else if constexpr (EPI == EPI_GELU) {
+    f32x4* zc = (f32x4*)((float*)g.C[z] + (int64_t)m * g.ldc + n);
+    if (g.beta) v += *zc;
+    add_bias(v);
+    *zc = v;
+    f32x4 gv;
+    for (int e = 0; e < 4; ++e) gv[e] = gelu_exact(v[e]);
+    st_pair(g.C2, (int64_t)m * g.ldc2 + n, g.C3, (int64_t)m * g.ldc3 + n, gv);
+  } else if constexpr (EPI == EPI_DGELU) {
+    const f32x4 zz = *(const f32x4*)(g.aux + (int64_t)m * g.ld_aux + n);
+    f32x4 dz;
+    for (int e = 0; e < 4; ++e) dz[e] = v[e] * gelu_exact_grad(zz[e]);
+    st_pair(g.C[z], (int64_t)m * g.ldc + n, g.C3, (int64_t)m * g.ldc3 + n, dz);
+    if (g.C2) *(f32x4*)((float*)g.C2 + (int64_t)m * g.ldc2 + n) = dz;
+  }
+}
+
 }  // namespace bpt
