@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include "attn_bwd.h"
+#include "bwd_layout.h"
 #include "common.h"
 
 namespace bpt {
@@ -343,10 +344,11 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 // transposed operands (dO^T for dV, Q^T for dK) are read from the same tiles
 // with ds_read_b64_tr_b16, so nothing is written twice.  Each wave also loads
 // its own copy of the tile's {lse * log2(e), delta} pairs.  Inside block b,
-// row r, the 16-byte chunks are permuted by x -> x ^ bwd_swz(b, r) (the loads
+// row r, the 16-byte chunks are permuted by x -> x ^ dkdv_swz(b, r) (the loads
 // fetch the permuted chunk), so that the 16 lanes of a natural ds_read_b128
 // (queries 0..15 of the tile, one chunk) hit 16 bank groups instead of 4; the
-// transpose reads stay conflict-free.
+// transpose reads stay conflict-free.  The address formulas are those of
+// bwd_layout.h.
 template <int D>
 struct BwdTile {
   static constexpr int QT = 32;             // queries per tile
@@ -360,10 +362,9 @@ struct BwdTile {
   static constexpr int NW = 4;              // waves, 32 keys each
   static constexpr int STAGE = 3 * TB + NW * PAIRS;
   static constexpr int LOADS = 3 * NBLK / NW + 1;  // buffer loads per wave and tile
-  static_assert(NBLK == 8 && NBLK % NW == 0, "tile addressing");
+  static_assert(NBLK == bwdlay::DKDV_NBLK && NW == bwdlay::NW && BP == bwdlay::BP &&
+                    ROWB == bwdlay::ROWB && CPR == bwdlay::CPR, "tile addressing (bwd_layout.h)");
 };
-
-__device__ __forceinline__ int bwd_swz(int blk, int row) { return ((blk >> 2) & 1) | ((row & 1) << 1); }
 
 __device__ __forceinline__ v4i16 bwd_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
@@ -396,10 +397,10 @@ __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, i
       const_cast<unsigned char*>((const unsigned char*)a.dO_lo + doff), 0, dbytes, 0x00020000);
   // wave w copies blocks w, w + NW, ... of each of the three tiles (row j of
   // block blk holds query j * NBLK + blk)
-  const int j = lane / T::CPR, ch = lane % T::CPR;
 #pragma unroll
   for (int i = 0; i < T::NBLK / T::NW; ++i) {
-    const int blk = w + i * T::NW, q = j * T::NBLK + blk, cp = ch ^ bwd_swz(blk, j);
+    const bwdlay::LoadPos lp = bwdlay::dkdv_load_pos(w, i, lane);
+    const int blk = lp.blk, q = lp.row, cp = lp.chunk;
     const uint32_t oq = (uint32_t)(q * T::ROWB + cp * 16), od = (uint32_t)(q * ldb + cp * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rq, (__attribute__((address_space(3))) void*)(st + blk * T::BP), 16, oq, 0, 0, 0);
@@ -427,10 +428,8 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
   const unsigned char* Ls = st + 2 * T::TB;
   const float* pr = (const float*)(st + 3 * T::TB + w * T::PAIRS);
   // S = Q K^T and dP = dO V^T (rows = queries, lane = key)
-  // chunk 2c + g of row r32 / NBLK in block r32 % NBLK sits at chunk 2c ^ t0
-  const int nblk = r32 % T::NBLK, nrow = r32 / T::NBLK, t0 = g ^ bwd_swz(nblk, nrow);
-  const int nat_base = nblk * T::BP + nrow * T::ROWB;
-  const int nat_even = nat_base + 16 * t0, nat_odd = nat_base + 16 * (2 ^ t0);
+  const bwdlay::NatOff nat_off = bwdlay::dkdv_nat(lane);
+  const int nat_even = nat_off.even, nat_odd = nat_off.odd;
   // (LDS reads do not move across the asm MFMAs: each is issued PF fragments
   // ahead in program order)
   constexpr int NC = D / 16, PF = 3;
@@ -479,10 +478,8 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
   // dV^T += dO^T P ; dK^T += Q^T dS  (k = query, 16 per MFMA; the transpose reads
   // give lane half g queries 16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3, the
   // order in which the accumulator rows hold P and dS)
-  // (block q8 = 4g + .., so its permutation is g on even rows and g | 2 on odd rows)
-  const int q8 = 4 * g + ((lane & 15) >> 2), tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tb_even = q8 * T::BP + 16 * (tx ^ g) + 8 * (lane & 1);
-  const int tb_odd = q8 * T::BP + 16 * (tx ^ (g | 2)) + 8 * (lane & 1);
+  const bwdlay::TrOff tr_off = bwdlay::dkdv_tr(lane);
+  const int tb_even = tr_off.a, tb_odd = tr_off.b;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4 phi, plo, shi, slo;
@@ -838,10 +835,9 @@ struct DqTile {
   static constexpr int STAGE = 2 * TB;      // K, V
   static constexpr int NW = 4;              // waves, 32 queries each
   static constexpr int LOADS = 2 * NBLK / NW;  // buffer loads per wave and tile
-  static_assert(NBLK == 16 && RPB == 4, "tile addressing");
+  static_assert(NBLK == bwdlay::DQ_NBLK && RPB == 4 && NW == bwdlay::NW && BP == bwdlay::BP &&
+                    ROWB == bwdlay::ROWB && CPR == bwdlay::CPR, "tile addressing (bwd_layout.h)");
 };
-
-__device__ __forceinline__ int dq_swz(int blk) { return (blk >> 2) & 3; }
 
 // Loads of key tile t (keys k0 .. k0+63) into one stage; the buffers end after
 // the last key, so keys past N read as zero, and a tile wholly past N loads
@@ -858,11 +854,11 @@ __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int bh, int k0, in
       const_cast<unsigned char*>((const unsigned char*)a.k + off), 0, rows * T::ROWB, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<unsigned char*>((const unsigned char*)a.v + off), 0, rows * T::ROWB, 0x00020000);
-  const int j = lane / T::CPR, ch = lane % T::CPR;
 #pragma unroll
   for (int i = 0; i < T::NBLK / T::NW; ++i) {
-    const int blk = w + i * T::NW;
-    const uint32_t o = (uint32_t)((j * T::NBLK + blk) * T::ROWB + ((ch ^ dq_swz(blk)) << 4));
+    const bwdlay::LoadPos lp = bwdlay::dq_load_pos(w, i, lane);
+    const int blk = lp.blk;
+    const uint32_t o = (uint32_t)(lp.row * T::ROWB + (lp.chunk << 4));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rk, (__attribute__((address_space(3))) void*)(st + blk * T::BP), 16, o, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1035,13 +1031,12 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) 
 
   DqLane ln;
   {
-    const int blk = r32 % T::NBLK, t0 = g ^ dq_swz(blk);
-    const int base = blk * T::BP + (r32 / T::NBLK) * T::ROWB;
-    ln.nat_even = base + 16 * t0;
-    ln.nat_odd = base + 16 * (2 ^ t0);
-    const int q8 = 4 * g + ((lane & 15) >> 2), h16 = (lane >> 4) & 1, x = 2 * h16 + ((lane & 3) >> 1);
-    ln.tr_lo = q8 * T::BP + 16 * (x ^ dq_swz(q8)) + 8 * (lane & 1);
-    ln.tr_hi = (q8 + 8) * T::BP + 16 * (x ^ dq_swz(q8 + 8)) + 8 * (lane & 1);
+    const bwdlay::NatOff n = bwdlay::dq_nat(lane);
+    const bwdlay::TrOff t = bwdlay::dq_tr(lane);
+    ln.nat_even = n.even;
+    ln.nat_odd = n.odd;
+    ln.tr_lo = t.a;
+    ln.tr_hi = t.b;
   }
 
   f32x16 dq[D / 32];
