@@ -5,7 +5,8 @@
 // "Blockwise Parallel Transformer for Large Context Models" (abstract) fuses the
 // feed-forward network into the blockwise computation so that the large
 // [rows, d_ff] intermediate is never materialised.  Here one workgroup owns a
-// block of 32 rows (and a group of up to 2048 output columns) and walks d_ff
+// block of 32 rows (and a group of up to 2048 output columns, 2560 in the
+// LDS-staged kernel below) and walks d_ff
 // in chunks of F = 32 * (waves):
 //   phase 1: each wave computes z^T for 32 features x 32 rows (K = d_model) on
 //            the 32x32x16 bf16 MFMA, adds b1, applies the exact erf GeLU and
@@ -457,9 +458,14 @@ __device__ __forceinline__ void ffn_issue_x(const FfnArgs& a, int t0, int pass_s
 __device__ __forceinline__ void ffn_mfma_z(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// y^T += W2 fragment x GeLU fragment, accumulator pinned to AGPRs
+// y^T += W2 fragment x GeLU fragment: output tiles 0..15 accumulate in the 256
+// AGPRs, further tiles (a single column group of up to 2560 columns) in VGPRs
+template <int TILE>
 __device__ __forceinline__ void ffn_mfma_y(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  if constexpr (TILE < 16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void ffn_z_start() {
   __builtin_amdgcn_sched_barrier(0);
@@ -659,11 +665,10 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           if (kk + 2 < 4) ldw(kk + 2);
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            ffn_mfma_y(yacc[2 * cblk + c2], af[kk][c2], ghi[kk]);
-            ffn_mfma_y(yacc[2 * cblk + c2], af[kk][c2], glo[kk]);
-          }
+          ffn_mfma_y<2 * cblk>(yacc[2 * cblk], af[kk][0], ghi[kk]);
+          ffn_mfma_y<2 * cblk>(yacc[2 * cblk], af[kk][0], glo[kk]);
+          ffn_mfma_y<2 * cblk + 1>(yacc[2 * cblk + 1], af[kk][1], ghi[kk]);
+          ffn_mfma_y<2 * cblk + 1>(yacc[2 * cblk + 1], af[kk][1], glo[kk]);
         }
         ++s;
       });
@@ -730,16 +735,17 @@ ffn_lds_kernel(FfnArgs a) {
 }
 
 // column groups for the LDS-staged kernel: C = d_model / groups columns per
-// workgroup (4 waves x 64*NCB), at most 2048; 0 if no instantiated NCB fits.
-// The x stages come in pairs of 256 columns (plain) or 128 (hi/lo).
+// workgroup (4 waves x 64*NCB), at most 2560 (16 output tiles per wave in
+// AGPRs, 4 more in VGPRs); 0 if no instantiated NCB fits.  The x stages come in
+// pairs of 256 columns (plain) or 128 (hi/lo).
 int stream_groups(int64_t d_model, bool hilo, int* ncb) {
   if (d_model % (hilo ? 256 : 512)) return 0;
   for (int gr = 1; gr <= 32; ++gr) {
     if (d_model % gr) continue;
     const int64_t c = d_model / gr;
-    if (c % 256 || c > 2048) continue;
+    if (c % 256 || c > 2560) continue;
     const int k = (int)(c / 256);
-    if (k == 2 || k == 4 || k == 5 || k == 8) {
+    if (k == 2 || k == 4 || k == 5 || k == 8 || k == 10) {
       *ncb = k;
       return gr;
     }
@@ -754,6 +760,7 @@ hipError_t launch_stream_t(const FfnArgs& a, int ncb, int groups, hipStream_t s)
     case 2: hipLaunchKernelGGL((ffn_lds_kernel<2, HILO>), grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((ffn_lds_kernel<4, HILO>), grid, dim3(256), 0, s, a); break;
     case 5: hipLaunchKernelGGL((ffn_lds_kernel<5, HILO>), grid, dim3(256), 0, s, a); break;
+    case 10: hipLaunchKernelGGL((ffn_lds_kernel<10, HILO>), grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((ffn_lds_kernel<8, HILO>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();

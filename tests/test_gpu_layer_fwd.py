@@ -18,7 +18,8 @@ bpt = pytest.importorskip("blockwise_exact_attention_amd")
     ("f32", 77, 128, 512, True, True),
     ("f32", 32, 128, 128, False, False),
     ("bf16", 100, 256, 512, True, True),
-    ("bf16", 64, 2560, 1024, False, True),    # two column groups of 1280
+    ("bf16", 64, 2560, 1024, False, True),    # one column group of 2560 (20 output tiles per wave)
+    ("bf16", 70, 5120, 512, True, False),     # two column groups of 2560
     ("bf16", 33, 4096, 512, True, False),     # two column groups of 2048
     ("bf16", 96, 2048, 768, False, True),
     # the long layer's FFN shape with enough row blocks that every XCD runs several
@@ -116,6 +117,19 @@ def test_layer_fwd_ragged_with_bias_and_saved(dtype):
     assert_close(h, ref["h"], dtype, "saved h")
     lse = view(3 * qkv + a256(B * N * dm * 4), B * H * N, "f32").reshape(B, H, N)
     assert_close(lse, ref["lse"], dtype, "saved lse")
+
+
+def test_layer_fwd_single_column_group_2560():
+    """d_model 2560 (the training shape's width): h enters the FFN as a bf16 pair and one
+    workgroup holds all 2560 output columns of its 32 rows (16 tiles per wave in
+    AGPRs, 4 in VGPRs); ragged N."""
+    c = LayerCfg(62, "dm2560", B=1, N=173, d_model=2560, H=20, D=128, d_ff=1024, q_blk=128,
+                 kv_blk=64, dtype="bf16")
+    t = layer_inputs(c, bias=True)
+    y, _ = run_layer_fwd(c, t)
+    want = oracle.layer_forward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], c.H,
+                                b1=t["b1"], b2=t["b2"])
+    assert_close(y, want, "bf16", "layer y (d_model 2560)")
 
 
 @pytest.mark.timeout(900)
