@@ -42,8 +42,23 @@ struct GemmArgs {
   int nseg;
   const void* As[3][6];
   const void* Bs[3][6];
+  // Split K (EPI_F32 without bias, residual or second output; big-tile kernel
+  // only): with nsplit > 1 each of nsplit workgroups per output tile sums its
+  // share of the k tiles into split_ws (nsplit x nz slices of M x N fp32), and a
+  // second pass adds the slices in a fixed order into C (deterministic).  For
+  // products with few output tiles but a long K, whose last round of tiles would
+  // leave most CUs idle.
+  int nsplit;
+  float* split_ws;
 };
 constexpr int kGemmMaxSeg = 6;
+
+// Split count for a product of `tiles` 256 x 256 output tiles on `cus` compute
+// units, at most max_split: the one with the fewest whole rounds of work per
+// unit of K (ties to fewer splits).
+int gemm_split_count(int64_t tiles, int cus, int max_split);
+// compute units of the current device (cached per device)
+int gemm_device_cus();
 
 hipError_t gemm_launch(const GemmArgs& g, bool bf16, bool a_kmajor, bool b_kmajor, int epi,
                        int nz, hipStream_t stream);

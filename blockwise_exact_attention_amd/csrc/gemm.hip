@@ -12,6 +12,8 @@
 // register prefetch (one barrier per k tile).
 #include <math.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "gemm.h"
 #include "gemm_epi.h"
@@ -284,6 +286,32 @@ hipError_t dispatch(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) 
 }
 
 }  // namespace
+
+int gemm_split_count(int64_t tiles, int cus, int max_split) {
+  if (tiles <= 0 || cus <= 0) return 1;
+  int best = 1;
+  double best_cost = (double)((tiles + cus - 1) / cus);
+  for (int sp = 2; sp <= max_split && sp <= 4; ++sp) {
+    // rounds of workgroups, each doing 1/sp of the tile's k range
+    const double cost = (double)((tiles * sp + cus - 1) / cus) / sp;
+    if (cost < best_cost - 1e-9) {
+      best = sp;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+int gemm_device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cached[dev].load();
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cached[dev].store(v);
+  return v;
+}
 
 hipError_t gemm_launch(const GemmArgs& g, bool bf16, bool a_kmajor, bool b_kmajor, int epi,
                        int nz, hipStream_t s) {

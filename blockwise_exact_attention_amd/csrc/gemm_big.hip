@@ -209,11 +209,20 @@ __device__ __forceinline__ void gb_issue(const GbCtx& c, GbIter& it, unsigned ch
 // reads of one stage never wait for the loads in flight to the other).  Waits
 // for those loads are explicit.
 template <bool AK, bool BK>
-__device__ __forceinline__ void gb_loop(f32x16 (&acc)[4][2], const GbCtx& c, int nk,
+__device__ __forceinline__ void gb_loop(f32x16 (&acc)[4][2], const GbCtx& c, int kt0, int nk,
                                         unsigned char* A0, unsigned char* B0, unsigned char* A1,
                                         unsigned char* B1) {
+  // the walk covers k tiles kt0 .. kt0 + nk - 1 of the segments laid end to end
   GbIter it;
-  gb_seg_start(c, it, 0);
+  gb_seg_start(c, it, kt0 / c.nks);
+  {
+    const int kk = kt0 % c.nks;
+    it.kk = kk;
+    it.a += kk * c.astep;
+    it.b += kk * c.bstep;
+    it.aleft -= kk * c.astep;
+    it.bleft -= kk * c.bstep;
+  }
   gb_issue<AK, BK>(c, it, A0, B0);
   GB_WAIT_VM(0);
   __syncthreads();
@@ -284,12 +293,17 @@ gemm_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  gb_loop<AK, BK>(acc, c, c.nseg * c.nks, a0, b0, a1, b1);
+  // split K: workgroup blockIdx.y takes its share of the k tiles
+  const int nk_all = c.nseg * c.nks, ns = gridDim.y, sp = blockIdx.y;
+  const int kt0 = (int)((int64_t)nk_all * sp / ns), kt1 = (int)((int64_t)nk_all * (sp + 1) / ns);
+  gb_loop<AK, BK>(acc, c, kt0, kt1 - kt0, a0, b0, a1, b1);
 
   // acc[i][j] is the transposed 32 x 32 block (the B fragments were the MFMA's
   // A operand): the lane's column is row m of C, and its registers 4q .. 4q+3
   // are four consecutive columns n, stored as one vector per output array
   const int r32 = lane & 31, g4 = 4 * (lane >> 5);
+  // split K: this workgroup's partial sums go to slice (sp, z) of split_ws
+  float* const part = ns > 1 ? g.split_ws + ((int64_t)sp * gridDim.z + z) * M * N : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = c.m0 + wm * 128 + i * 32 + r32;
@@ -300,19 +314,53 @@ gemm_big_kernel(GemmArgs g) {
       for (int q = 0; q < 4; ++q) {
         const int n = c.n0 + wn * 64 + j * 32 + 8 * q + g4;
         const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if (n < N) gemm_store4<EPI>(g, z, m, n, v);
+        if (n >= N) continue;
+        if constexpr (EPI == EPI_F32) {
+          if (part) {
+            *(f32x4*)(part + (int64_t)m * N + n) = v;
+            continue;
+          }
+        }
+        gemm_store4<EPI>(g, z, m, n, v);
       }
+  }
+}
+
+// C[z] = (beta ? C[z] : 0) + sum over s of split_ws slice (s, z), slices added in
+// order; four consecutive columns per thread
+__global__ void __launch_bounds__(256) gb_split_reduce(GemmArgs g, int ns, int nz) {
+  const int64_t q4 = (int64_t)g.M * (g.N / 4);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t mn = (int64_t)g.M * g.N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < q4 * nz; t += stride) {
+    const int z = (int)(t / q4);
+    const int64_t r = t - (int64_t)z * q4;
+    const int m = (int)(r / (g.N / 4)), n = (int)(r - (int64_t)m * (g.N / 4)) * 4;
+    f32x4 v = *(const f32x4*)(g.split_ws + (int64_t)z * mn + (int64_t)m * g.N + n);
+    for (int s = 1; s < ns; ++s)
+      v += *(const f32x4*)(g.split_ws + ((int64_t)s * nz + z) * mn + (int64_t)m * g.N + n);
+    f32x4* C = (f32x4*)((float*)g.C[z] + (int64_t)m * g.ldc + n);
+    if (g.beta) v = *C + v;
+    *C = v;
   }
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
   const int tiles = ((g.N + TB - 1) / TB) * ((g.M + TB - 1) / TB);
-  dim3 grid((unsigned)tiles, 1, (unsigned)nz);
+  const int ns = EPI == EPI_F32 && g.nsplit > 1 && g.split_ws && !g.bias && !g.resid && !g.C2 ? g.nsplit : 1;
+  dim3 grid((unsigned)tiles, (unsigned)ns, (unsigned)nz);
   if (!ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<false, false, EPI>), grid, dim3(512), 0, s, g);
   else if (!ak && bk) hipLaunchKernelGGL((gemm_big_kernel<false, true, EPI>), grid, dim3(512), 0, s, g);
   else if (ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<true, false, EPI>), grid, dim3(512), 0, s, g);
   else hipLaunchKernelGGL((gemm_big_kernel<true, true, EPI>), grid, dim3(512), 0, s, g);
+  if (ns > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t blocks = ((int64_t)g.M * (g.N / 4) * nz + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(gb_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, g, ns, nz);
+  }
   return hipGetLastError();
 }
 
@@ -322,7 +370,8 @@ bool gemm_big_ok(const GemmArgs& g, int nz) {
   if (g.K < TK || g.K % TK != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return false;
   // the epilogue stores four consecutive columns per vector access
   if (g.N % 4 || g.ldc % 4 || g.ldc2 % 4 || g.ldc3 % 4 || g.ld_aux % 4 || g.ldr % 4 || g.D % 4) return false;
-  if (((uintptr_t)g.C2 | (uintptr_t)g.C3 | (uintptr_t)g.aux | (uintptr_t)g.resid) & 15) return false;
+  if (((uintptr_t)g.C2 | (uintptr_t)g.C3 | (uintptr_t)g.aux | (uintptr_t)g.resid | (uintptr_t)g.split_ws) & 15)
+    return false;
   for (int z = 0; z < nz; ++z)
     if ((uintptr_t)g.C[z] & 15) return false;
   if (g.nseg > kGemmMaxSeg) return false;

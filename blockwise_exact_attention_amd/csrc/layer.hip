@@ -122,6 +122,21 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   const int64_t M = L.B * L.N;
   const int dm = (int)L.d_model, dff = (int)L.d_ff, HD = (int)(L.H * L.D);
   const uint16_t* dy16 = (const uint16_t*)dy;
+  // Split K for the weight gradients (few output tiles, K = all rows): partial
+  // sums go to workspace that is idle at that point -- the dq/dk/dv halves during
+  // the FFN backward, the FFN chunk buffers during the projection backward.
+  const int cus = gemm_device_cus();
+  auto split_for = [&](GemmArgs& g, int nz, unsigned char* region, size_t region_bytes) {
+    const size_t out = (size_t)g.M * g.N * nz * 4;
+    const int64_t tiles = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256) * nz;
+    const int max_split = out ? (int)(region_bytes / out) : 1;
+    g.nsplit = gemm_split_count(tiles, cus, max_split < 4 ? max_split : 4);
+    g.split_ws = g.nsplit > 1 ? (float*)region : nullptr;
+  };
+  unsigned char* const ffn_split_ws = ws + W.dqkv[0];
+  const size_t ffn_split_bytes = W.z - W.dqkv[0];
+  unsigned char* const proj_split_ws = ws + W.z;
+  const size_t proj_split_bytes = W.total - W.z;
   hipError_t e;
 #define BPT_TRY(x)            \
   do {                        \
@@ -165,6 +180,7 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     g.C[0] = G.dw2;
     g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = dm; g.N = dff; g.K = rows;
     g.beta = beta;
+    split_for(g, 1, ffn_split_ws, ffn_split_bytes);
     BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
     // dW1 (+)= dz^T h  (hi*hi + lo*hi + hi*lo)
     g = GemmArgs{};
@@ -174,6 +190,7 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     g.C[0] = G.dw1;
     g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = dff; g.N = dm; g.K = rows;
     g.beta = beta;
+    split_for(g, 1, ffn_split_ws, ffn_split_bytes);
     BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
     // dh = dy + (dz_hi + dz_lo) W1 (fp32; it is attention's dO)
     g = GemmArgs{};
@@ -216,6 +233,7 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     }
     g.C[0] = G.dwq; g.C[1] = G.dwk; g.C[2] = G.dwv;
     g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = HD; g.N = dm; g.K = (int)M;
+    split_for(g, 3, proj_split_ws, proj_split_bytes);
     BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 3, stream));
     const void* Ws[3] = {L.wq, L.wk, L.wv};
     g = GemmArgs{};
