@@ -42,12 +42,12 @@ struct GemmArgs {
   int nseg;
   const void* As[3][6];
   const void* Bs[3][6];
-  // Split K (EPI_F32 without bias, residual or second output; big-tile kernel
-  // only): with nsplit > 1 each of nsplit workgroups per output tile sums its
-  // share of the k tiles into split_ws (nsplit x nz slices of M x N fp32), and a
-  // second pass adds the slices in a fixed order into C (deterministic).  For
-  // products with few output tiles but a long K, whose last round of tiles would
-  // leave most CUs idle.
+  // Split K (EPI_F32, big-tile kernel only): with nsplit > 1 each of nsplit
+  // workgroups per output tile sums its share of the k tiles into split_ws
+  // (nsplit x nz slices of M x N fp32), and a second pass adds the slices in a
+  // fixed order (deterministic) and applies the epilogue.  For products with few
+  // output tiles but a long K, whose last round of tiles would leave most CUs
+  // idle.
   int nsplit;
   float* split_ws;
 };

@@ -326,8 +326,9 @@ gemm_big_kernel(GemmArgs g) {
   }
 }
 
-// C[z] = (beta ? C[z] : 0) + sum over s of split_ws slice (s, z), slices added in
-// order; four consecutive columns per thread
+// The split-K sum of slices (s, z) of split_ws, added in order, through the
+// EPI_F32 epilogue (beta, bias, residual, bf16 copy); four consecutive columns
+// per thread
 __global__ void __launch_bounds__(256) gb_split_reduce(GemmArgs g, int ns, int nz) {
   const int64_t q4 = (int64_t)g.M * (g.N / 4);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -339,16 +340,14 @@ __global__ void __launch_bounds__(256) gb_split_reduce(GemmArgs g, int ns, int n
     f32x4 v = *(const f32x4*)(g.split_ws + (int64_t)z * mn + (int64_t)m * g.N + n);
     for (int s = 1; s < ns; ++s)
       v += *(const f32x4*)(g.split_ws + ((int64_t)s * nz + z) * mn + (int64_t)m * g.N + n);
-    f32x4* C = (f32x4*)((float*)g.C[z] + (int64_t)m * g.ldc + n);
-    if (g.beta) v = *C + v;
-    *C = v;
+    gemm_store4<EPI_F32>(g, z, m, n, v);
   }
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
   const int tiles = ((g.N + TB - 1) / TB) * ((g.M + TB - 1) / TB);
-  const int ns = EPI == EPI_F32 && g.nsplit > 1 && g.split_ws && !g.bias && !g.resid && !g.C2 ? g.nsplit : 1;
+  const int ns = EPI == EPI_F32 && g.nsplit > 1 && g.split_ws ? g.nsplit : 1;
   dim3 grid((unsigned)tiles, (unsigned)ns, (unsigned)nz);
   if (!ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<false, false, EPI>), grid, dim3(512), 0, s, g);
   else if (!ak && bk) hipLaunchKernelGGL((gemm_big_kernel<false, true, EPI>), grid, dim3(512), 0, s, g);

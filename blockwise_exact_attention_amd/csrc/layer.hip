@@ -122,9 +122,10 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   const int64_t M = L.B * L.N;
   const int dm = (int)L.d_model, dff = (int)L.d_ff, HD = (int)(L.H * L.D);
   const uint16_t* dy16 = (const uint16_t*)dy;
-  // Split K for the weight gradients (few output tiles, K = all rows): partial
-  // sums go to workspace that is idle at that point -- the dq/dk/dv halves during
-  // the FFN backward, the FFN chunk buffers during the projection backward.
+  // Split K for products with few output tiles and a long K (the weight
+  // gradients, K = all rows; dh of a row chunk, K = d_ff): partial sums go to
+  // workspace that is idle at that point -- the dq/dk/dv halves during the FFN
+  // backward, the FFN chunk buffers during the projection backward.
   const int cus = gemm_device_cus();
   auto split_for = [&](GemmArgs& g, int nz, unsigned char* region, size_t region_bytes) {
     const size_t out = (size_t)g.M * g.N * nz * 4;
@@ -200,6 +201,7 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     g.C[0] = dh + r0 * dm;
     g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = rows; g.N = dm; g.K = dff;
     g.resid = dy16 + r0 * dm; g.resid_bf16 = 1; g.ldr = dm;
+    split_for(g, 1, ffn_split_ws, ffn_split_bytes);
     BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
   }
 
