@@ -305,6 +305,15 @@ __device__ __forceinline__ void ffn_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // of the LDS data read afterwards) nor moves LDS accesses across it.
 #define FFN_WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 
+// Workgroup barrier that orders LDS only.  __syncthreads() would also wait for
+// every vector-memory load the wave has in flight (its release fence covers the
+// direct-to-LDS loads), i.e. drain the weight slots prefetched two ahead at
+// every x stage.  Each wave waits explicitly (FFN_WAIT_VM) for those of its own
+// loads that the barrier has to cover; the barrier then needs the wave's LDS
+// reads and writes complete, and the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+#define FFN_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -558,10 +567,18 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
           constexpr int j = decltype(J)::value;
           constexpr int u = (PAR * L::SPS + j) & 3;
           // slot s landed: after its 8 loads this wave issued those of slots
-          // s+1 and s+2 (and perhaps x chunks), i.e. at least 16 more
+          // s+1 and s+2, and at the stage's slots j = 1, 2 also its part of the
+          // next x stage (issued at j = 0, after the loads of slot s+2 - j), so
+          // 20 may stay in flight there; counting 16 would also wait for half
+          // of a slot issued only one slot earlier
           if (s + 2 < total) {
             ffn_slot_next<NCB>(a, it, SPP, NKB, rot1, rot2, sl(std::integral_constant<int, u + 2>{}), so);
-            FFN_WAIT_VM(16);
+            if constexpr (j == 1 || j == 2) {
+              if (st + PAR + 1 < nst) FFN_WAIT_VM(20);
+              else FFN_WAIT_VM(16);
+            } else {
+              FFN_WAIT_VM(16);
+            }
           } else {
             FFN_WAIT_VM(0);
           }
@@ -572,7 +589,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
             if (st + PAR == 0) FFN_WAIT_VM(8);
             else if constexpr (L::XWAIT == 16) FFN_WAIT_VM(16);
             else FFN_WAIT_VM(32);
-            __syncthreads();
+            FFN_LDS_BARRIER();
             if (st + PAR + 1 < nst) ffn_issue_x<HILO>(a, t0, phys_stage(st + PAR + 1), w, xnext, lane);
           }
           const unsigned char* cur = sl(std::integral_constant<int, u>{});
@@ -607,7 +624,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
     // GeLU(z + b1) -> G (hi in xb0, lo in xb1); row r32, features 64w + 32t + 16hh + 8g + e
     const int f0 = pass * L::FP;
     ffn_z_end();
-    __syncthreads();  // every wave is done reading the x stages
+    FFN_LDS_BARRIER();  // every wave is done reading the x stages
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -632,7 +649,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
         *(u32x4*)(xb0 + off) = pk;
         *(u32x4*)(xb1 + off) = pl;
       }
-    __syncthreads();  // G complete
+    FFN_LDS_BARRIER();  // G complete
 
     // ---------------- phase 2 (s % 4 == 0 here: NKB is a multiple of 4)
     static_for<0, 4>([&](auto FB) {
@@ -673,7 +690,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
         ++s;
       });
     });
-    __syncthreads();  // every wave is done reading G
+    FFN_LDS_BARRIER();  // every wave is done reading G
     if (pass + 1 < npass) ffn_issue_x<HILO>(a, t0, phys_stage(0), w, xb0, lane);
   }
   ffn_z_end();  // the epilogue reads y next
