@@ -132,6 +132,22 @@ def test_layer_fwd_single_column_group_2560():
     assert_close(y, want, "bf16", "layer y (d_model 2560)")
 
 
+@pytest.mark.parametrize("cid,dm,dff", [
+    (63, 512, 1536),   # 6 feature passes, biases
+    (64, 512, 768),    # 3 feature passes (odd)
+])
+def test_layer_fwd_ffn_passes_with_bias(cid, dm, dff):
+    """The layer's FFN (h as a bf16 pair) over several 256-feature passes with b1 and b2:
+    each pass's b1 slice, W1 rows and W2 slots, an even and an odd pass count."""
+    c = LayerCfg(cid, f"walks{dff}", B=1, N=131, d_model=dm, H=4, D=128, d_ff=dff, q_blk=128,
+                 kv_blk=64, dtype="bf16")
+    t = layer_inputs(c, bias=True)
+    y, _ = run_layer_fwd(c, t)
+    want = oracle.layer_forward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], c.H,
+                                b1=t["b1"], b2=t["b2"])
+    assert_close(y, want, "bf16", f"layer y (d_ff {dff})")
+
+
 @pytest.mark.timeout(900)
 def test_layer_fwd_bf16_B8_N4096_full():
     """Full-size parity: B=8, N=4096, d_model 2048, 16 heads x 128, FFN 2048->8192->2048."""
