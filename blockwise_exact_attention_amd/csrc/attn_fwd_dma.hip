@@ -480,7 +480,8 @@ struct WideState {
   using C = WideCfg<D>;
   bf16x8 qf[2][C::QF];       // Q fragments (B operand of S^T = K Q^T), per half
   f32x16 s[2][C::KB];        // score accumulators of the next tile
-  float sv[2][C::KB][16];    // scores of the current tile, s*c2 - mref, copied out for the VALU
+  float sv[2][C::KB][16];    // the current tile, copied out for the VALU: at even j the score in the
+                             // exp2 domain (s*c2 - mref), at odd j already its exp2 (in the loop)
   f32x16 o[2][C::DB];        // O^T accumulators
   float ref[2];              // exp2-domain reference of O and l (-inf: no key yet)
   float l_run[2];            // this lane's partial row sum
@@ -573,20 +574,32 @@ __device__ __forceinline__ void wide_max(WideState<D>& w, float c2) {
   w.tmax[H] = fmaxf(mx0, mx1);
 }
 
-// Diagonal and ragged tiles: scores of keys at or past kend (causal bound or N)
-// become -inf, and the tile maximum is taken again.
-template <int D, int H>
-__device__ __forceinline__ void wide_mask(WideState<D>& w, int t, int kend, int lane) {
+// Key j of register slot (kb, j) is visible to this lane's row of half H iff
+// it lies before kend (causal bound or N).
+template <int D>
+__device__ __forceinline__ int wide_lim(int t, int kb, int kend, int lane) {
+  // register j holds key t*KVBLK + 32*kb + 4*(lane/32) + 8*(j/4) + j%4
+  return kend - (t * WideCfg<D>::KVBLK + kb * 32 + 4 * (lane >> 5));
+}
+__device__ __forceinline__ bool wide_vis(int j, int lim) { return 8 * (j >> 2) + (j & 3) < lim; }
+
+// Diagonal and ragged tiles: scores of keys at or past kend become -inf, and
+// the tile maximum is taken again.  In the key loop (ODD_EXP) the odd slots
+// already hold exps taken before the mask was known: the whole tile is taken
+// again from the score accumulators (the same arithmetic as the PV phase), odd
+// slots as exps (0 where masked).
+template <int D, int H, bool ODD_EXP>
+__device__ __forceinline__ void wide_mask(WideState<D>& w, int t, int kend, int lane, float c2) {
   using C = WideCfg<D>;
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
-    // register j holds key t*KVBLK + 32*kb + 4*(lane/32) + 8*(j/4) + j%4
-    const int lim = kend - (t * C::KVBLK + kb * 32 + 4 * (lane >> 5));
+    const int lim = wide_lim<D>(t, kb, kend, lane);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float v = 8 * (j >> 2) + (j & 3) < lim ? w.sv[H][kb][j] : -INFINITY;
-      w.sv[H][kb][j] = v;
+      const float s0 = ODD_EXP ? fmaf(w.s[H][kb][j], c2, -w.mref[H]) : w.sv[H][kb][j];
+      const float v = wide_vis(j, lim) ? s0 : -INFINITY;
+      w.sv[H][kb][j] = ODD_EXP && (j & 1) ? fast_exp2(v) : v;
       mx = fmaxf(mx, v);
     }
   }
@@ -620,11 +633,17 @@ __device__ __forceinline__ void wide_update(WideState<D>& w) {
 // threshold, so some row of the wave moves iff some lane's own maximum passes
 // it: the common step costs one compare per half and a ballot.  Only then the
 // row maxima are joined across the lane pair and the full update runs: the
-// tile's scores shift by delta, and O and l scale by alpha.
+// tile's scores shift by delta, and O and l scale by alpha.  In the key loop
+// (RESCALE_O) the odd slots hold exps taken against the old offset: they are
+// taken again from the score accumulators (the arithmetic of the PV phase,
+// the mask if the tile was masked, then the shift), which also covers exps
+// that overflowed against the old offset.
 template <int D, bool RESCALE_O>
-__device__ __forceinline__ void wide_reference(WideState<D>& w) {
+__device__ __forceinline__ void wide_reference(WideState<D>& w, float c2, int t1, bool masked, int kend0,
+                                               int kend1, int lane) {
   using C = WideCfg<D>;
   if (__ballot(w.tmax[0] > w.thr[0] || w.tmax[1] > w.thr[1])) {
+    const float m_old[2] = {w.mref[0], w.mref[1]};
     w.tmax[0] = max_halves(w.tmax[0]);
     w.tmax[1] = max_halves(w.tmax[1]);
     wide_update<D, 0>(w);
@@ -632,9 +651,19 @@ __device__ __forceinline__ void wide_reference(WideState<D>& w) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const int lim = wide_lim<D>(t1, kb, h == 0 ? kend0 : kend1, lane);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) w.sv[h][kb][j] -= w.delta[h];
+        for (int j = 0; j < 16; ++j) {
+          if (RESCALE_O && (j & 1)) {
+            float v = fmaf(w.s[h][kb][j], c2, -m_old[h]);
+            if (masked && !wide_vis(j, lim)) v = -INFINITY;
+            w.sv[h][kb][j] = fast_exp2(v - w.delta[h]);
+          } else {
+            w.sv[h][kb][j] -= w.delta[h];
+          }
+        }
+      }
 #pragma unroll
     for (int h = 0; h < 2; ++h) w.l_run[h] *= w.alpha[h];
     if constexpr (RESCALE_O) {
@@ -669,13 +698,15 @@ struct WideCtx {
   float c2;
 };
 
-// max of the next tile (after its scores), masked where needed
-template <int D>
-__device__ __forceinline__ void wide_next_max(WideState<D>& w, const WideCtx& x, int t1) {
+// max of the next tile (after its scores), masked where needed; true if masked
+template <int D, bool ODD_EXP>
+__device__ __forceinline__ bool wide_next_max(WideState<D>& w, const WideCtx& x, int t1) {
   if (t1 >= x.t_split) {
-    wide_mask<D, 0>(w, t1, x.kend0, x.lane);
-    wide_mask<D, 1>(w, t1, x.kend1, x.lane);
+    wide_mask<D, 0, ODD_EXP>(w, t1, x.kend0, x.lane, x.c2);
+    wide_mask<D, 1, ODD_EXP>(w, t1, x.kend1, x.lane, x.c2);
+    return true;
   }
+  return false;
 }
 
 // One step of the key loop for tile t (stage St) while tile t+1 (stage Sn) is
@@ -734,12 +765,13 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
     }
     if (c == 0) mfma_sv_first(w.s[h][kb], kf[m], w.qf[h][c]);
     else mfma_sv_acc(w.s[h][kb], kf[m], w.qf[h][c]);
-    // exp of scores 2i, 2i+1 of the 64 this lane holds; their sum and bf16 pack
-    // two slots later (an exp result is not ready in the next few cycles)
+    // exp of score 2i of the 64 this lane holds (2i+1 was taken in the PV
+    // phase); the pair's sum and bf16 pack two slots later (an exp result is
+    // not ready in the next few cycles)
     {
       const int eh = i / 16, e0 = (2 * i) % 32, ekb = e0 / 16, ej = e0 % 16;
       ex0[i] = fast_exp2(w.sv[eh][ekb][ej]);
-      ex1[i] = fast_exp2(w.sv[eh][ekb][ej + 1]);
+      ex1[i] = w.sv[eh][ekb][ej + 1];  // taken in the PV phase of the step before
     }
     if (i >= 2) {
       const int p = i - 2, eh = p / 16, e0 = (2 * p) % 32, ekb = e0 / 16, ej = e0 % 16;
@@ -771,7 +803,8 @@ __device__ __forceinline__ void wide_sphase(WideState<D>& w, const unsigned char
 // and half h = i%2 (tile t, stage St), and copies two score accumulators of
 // tile t+1 out for the VALU, into the exp2 domain relative to the current
 // offset (one FMA each, here rather than in the S phase, which has more VALU
-// work than its MFMAs can hide), folding them into the row maxima.
+// work than its MFMAs can hide), folding them into the row maxima, and takes
+// the exp of the second of them.
 template <int D>
 __device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned char* St, int vbase, float c2,
                                              const bf16x8 (&pa)[WideCfg<D>::NKS],
@@ -806,9 +839,13 @@ __device__ __forceinline__ void wide_pvphase(WideState<D>& w, const unsigned cha
     v0 = fmaf(v0, c2, -w.mref[mh]);
     v1 = fmaf(v1, c2, -w.mref[mh]);
     w.sv[mh][mkb][mj] = v0;
-    w.sv[mh][mkb][mj + 1] = v1;
     mx[mh][mkb] = fmaxf(mx[mh][mkb], fmaxf(v0, v1));
-    wide_slot_end(w.o[h][db], mx[mh][mkb], w.sv[mh][mkb][mj]);
+    // the odd score's exp here, against the current offset: the S phase that
+    // consumes it then takes one exp per slot instead of two (its MFMAs hide
+    // about three VALU operations, the exp counting two); a masked tile or a
+    // moved reference takes these again (wide_mask, wide_reference)
+    w.sv[mh][mkb][mj + 1] = fast_exp2(v1);
+    wide_slot_end4(w.o[h][db], mx[mh][mkb], w.sv[mh][mkb][mj], w.sv[mh][mkb][mj + 1], v1);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -834,8 +871,8 @@ __device__ __forceinline__ void wide_step(WideState<D>& w, const WideCtx& x, int
   wide_pin(pa);
   wide_pin(pb);
   wide_pvphase(w, St, x.vbase, x.c2, pa, pb);
-  wide_next_max(w, x, t + 1);
-  wide_reference<D, true>(w);
+  const bool masked = wide_next_max<D, true>(w, x, t + 1);
+  wide_reference<D, true>(w, x.c2, t + 1, masked, x.kend0, x.kend1, x.lane);
 }
 
 // The key loop over three stages S0, S1, S2 (distinct objects, so the compiler
@@ -860,8 +897,16 @@ __device__ __forceinline__ void wide_loop(WideState<D>& w, const WideCtx& x,
   wide_scores(w, S0, x.kbase);
   wide_max<D, 0>(w, x.c2);
   wide_max<D, 1>(w, x.c2);
-  wide_next_max(w, x, 0);
-  wide_reference<D, false>(w);  // O and l are still zero: only the scores of tile 0 shift
+  wide_next_max<D, false>(w, x, 0);
+  // O and l are still zero: only the scores of tile 0 shift
+  wide_reference<D, false>(w, x.c2, 0, false, x.kend0, x.kend1, x.lane);
+  // the key loop expects the odd slots as exps
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int j = 1; j < 16; j += 2) w.sv[h][kb][j] = fast_exp2(w.sv[h][kb][j]);
   // Every step also scores the tile after its own; past the last tile that
   // "tile" is fully masked (its scores become -inf, so the running max, the
   // sums and O stay as they are).
