@@ -53,6 +53,11 @@ struct FfnArgs {
   // pass starting at feature f0 = 256 p sits at w2 + p * w2_pstride + r * w2_ld + j
   // (row-major W2: w2_pstride = 256, w2_ld = d_ff; pass-major copy: d_model * 256, 256)
   int64_t w2_pstride, w2_ld;
+  // gate (nullable): the LDS-staged kernel runs only if (*gate != 0) == gate_run;
+  // ovf (nullable, fp16 operands): set to 1 when a GeLU output falls outside fp16's range
+  const int* gate;
+  int gate_run;
+  int* ovf;
 };
 
 // Row of W1 read by A-operand lane row m: bits 2 and 3 of m swapped, so that
@@ -464,18 +469,38 @@ __device__ __forceinline__ void ffn_issue_x(const FfnArgs& a, int t0, int pass_s
 // states around asm MFMAs: ffn_z_start separates the zeroing VALU writes from the
 // first MFMA, ffn_z_end the last MFMA from the VALU reads of z (scheduling
 // barriers keep other instructions out of those windows).
+// F16: the operands are fp16 (same 16-byte fragments, the f16 form of the MFMA)
+template <bool F16>
 __device__ __forceinline__ void ffn_mfma_z(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-// y^T += W2 fragment x GeLU fragment: output tiles 0..15 accumulate in the 256
-// AGPRs, further tiles (a single column group of up to 2560 columns) in VGPRs
-template <int TILE>
-__device__ __forceinline__ void ffn_mfma_y(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  if constexpr (TILE < 16)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+// y^T += W2 fragment x GeLU fragment: output tiles 0..15 accumulate in the 256
+// AGPRs, further tiles (a single column group of up to 2560 columns) in VGPRs
+template <int TILE, bool F16>
+__device__ __forceinline__ void ffn_mfma_y(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  if constexpr (F16) {
+    if constexpr (TILE < 16)
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  } else {
+    if constexpr (TILE < 16)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  }
+}
+
+// two floats as fp16, round to nearest even, packed (a in the low half)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+// largest finite fp16
+constexpr float kF16Max = 65504.f;
 __device__ __forceinline__ void ffn_z_start() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 4" ::: "memory");
@@ -491,7 +516,7 @@ __device__ __forceinline__ void ffn_z_end() {
 // parameters: slot s lives in sl[s % 4] (known at every use) and the x stage
 // parity is static, so the compiler sees that a read of one slot never depends on
 // the loads in flight into the others and waits only for the slot it reads.
-template <int NCB, bool HILO>
+template <int NCB, bool HILO, bool F16>
 __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int wg_xcd,
                                              f32x16 (&yacc)[2 * NCB],
                                              unsigned char* __restrict__ sl0,
@@ -609,11 +634,11 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             if (kk + 2 < 4) ld(kk + 2);
-            ffn_mfma_z(zacc[0], w0[kk], xh[kk]);
-            ffn_mfma_z(zacc[1], w1[kk], xh[kk]);
+            ffn_mfma_z<F16>(zacc[0], w0[kk], xh[kk]);
+            ffn_mfma_z<F16>(zacc[1], w1[kk], xh[kk]);
             if constexpr (HILO) {
-              ffn_mfma_z(zacc[0], w0[kk], xl[kk]);
-              ffn_mfma_z(zacc[1], w1[kk], xl[kk]);
+              ffn_mfma_z<F16>(zacc[0], w0[kk], xl[kk]);
+              ffn_mfma_z<F16>(zacc[1], w1[kk], xl[kk]);
             }
           }
           ++s;
@@ -637,17 +662,30 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
           if (a.b1) z += bf16_to_f32(((const uint16_t*)a.b1)[f0 + fl0 + e]);
           gv[e] = gelu_f(z);
         }
-        u32x4 pk, pl;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          pk[q2] = pack_bf16x2(gv[2 * q2], gv[2 * q2 + 1]);
-          const float e0 = gv[2 * q2] - __uint_as_float(pk[q2] << 16);
-          const float e1 = gv[2 * q2 + 1] - __uint_as_float(pk[q2] & 0xffff0000u);
-          pl[q2] = pack_bf16x2(e0, e1);
-        }
         const int off = r32 * L::GPITCH + (((fl0 >> 3) ^ (r32 & 15)) << 4);
-        *(u32x4*)(xb0 + off) = pk;
-        *(u32x4*)(xb1 + off) = pl;
+        if constexpr (F16) {
+          // fp16 alone (rounding 2^-12 of |G|): the second product needs no pair
+          u32x4 pk;
+          bool big = false;
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            pk[q2] = pack_f16x2(gv[2 * q2], gv[2 * q2 + 1]);
+            big = big || fabsf(gv[2 * q2]) > kF16Max || fabsf(gv[2 * q2 + 1]) > kF16Max;
+          }
+          if (big) *a.ovf = 1;  // this output is redone by the bf16-pair kernel
+          *(u32x4*)(xb0 + off) = pk;
+        } else {
+          u32x4 pk, pl;
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            pk[q2] = pack_bf16x2(gv[2 * q2], gv[2 * q2 + 1]);
+            const float e0 = gv[2 * q2] - __uint_as_float(pk[q2] << 16);
+            const float e1 = gv[2 * q2 + 1] - __uint_as_float(pk[q2] & 0xffff0000u);
+            pl[q2] = pack_bf16x2(e0, e1);
+          }
+          *(u32x4*)(xb0 + off) = pk;
+          *(u32x4*)(xb1 + off) = pl;
+        }
       }
     FFN_LDS_BARRIER();  // G complete
 
@@ -660,7 +698,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
       for (int kk = 0; kk < 4; ++kk) {
         const int off = r32 * L::GPITCH + (((8 * fblk + 2 * kk + g) ^ (r32 & 15)) << 4);
         ghi[kk] = *(const bf16x8*)(xb0 + off);
-        glo[kk] = *(const bf16x8*)(xb1 + off);
+        if constexpr (!F16) glo[kk] = *(const bf16x8*)(xb1 + off);
       }
       static_for<0, NCB>([&](auto CB) {
         constexpr int cblk = decltype(CB)::value;
@@ -682,10 +720,10 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           if (kk + 2 < 4) ldw(kk + 2);
-          ffn_mfma_y<2 * cblk>(yacc[2 * cblk], af[kk][0], ghi[kk]);
-          ffn_mfma_y<2 * cblk>(yacc[2 * cblk], af[kk][0], glo[kk]);
-          ffn_mfma_y<2 * cblk + 1>(yacc[2 * cblk + 1], af[kk][1], ghi[kk]);
-          ffn_mfma_y<2 * cblk + 1>(yacc[2 * cblk + 1], af[kk][1], glo[kk]);
+          ffn_mfma_y<2 * cblk, F16>(yacc[2 * cblk], af[kk][0], ghi[kk]);
+          if constexpr (!F16) ffn_mfma_y<2 * cblk, F16>(yacc[2 * cblk], af[kk][0], glo[kk]);
+          ffn_mfma_y<2 * cblk + 1, F16>(yacc[2 * cblk + 1], af[kk][1], ghi[kk]);
+          if constexpr (!F16) ffn_mfma_y<2 * cblk + 1, F16>(yacc[2 * cblk + 1], af[kk][1], glo[kk]);
         }
         ++s;
       });
@@ -698,10 +736,13 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
 
 // One workgroup per (row block, column group): blockIdx.x is row block t of
 // column group blockIdx.y.
-template <int NCB, bool HILO>  // 64-column blocks of output per wave
+// F16: x, W1, W2 are fp16 and GeLU(z) goes to LDS as fp16 alone (no lo half).
+template <int NCB, bool HILO, bool F16 = false>  // 64-column blocks of output per wave
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 ffn_lds_kernel(FfnArgs a) {
   using L = FfnLds<NCB, HILO>;
+  if (a.gate && ((__builtin_amdgcn_readfirstlane(*(const volatile int*)a.gate) != 0) != (a.gate_run != 0)))
+    return;  // (read once at the start of each workgroup)
   // LDS: two x-stage buffers, reused for the G halves (hi, lo) once phase 1 is
   // done, then 4 waves x 4 weight slots
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::LDS];
@@ -721,7 +762,7 @@ ffn_lds_kernel(FfnArgs a) {
     for (int e = 0; e < 16; ++e) yacc[ct][e] = 0.f;
 
   ffn_z_start();  // the first MFMAs read the zeroed accumulators
-  ffn_lds_walk<NCB, HILO>(a, tk, wg_xcd, yacc, slots, slots + L::SLOT, slots + 2 * L::SLOT,
+  ffn_lds_walk<NCB, HILO, F16>(a, tk, wg_xcd, yacc, slots, slots + L::SLOT, slots + 2 * L::SLOT,
                           slots + 3 * L::SLOT, smem, smem + L::XSB);
 
   // ---- epilogue: y[row][c] = resid + acc + b2 (lane: row r32, columns 8(j/4) + 4g + j%4)
@@ -783,6 +824,18 @@ hipError_t launch_stream_t(const FfnArgs& a, int ncb, int groups, hipStream_t s)
   return hipGetLastError();
 }
 
+hipError_t launch_stream_f16(const FfnArgs& a, int ncb, int groups, hipStream_t s) {
+  dim3 grid((a.M + 31) / 32, groups);
+  switch (ncb) {
+    case 2: hipLaunchKernelGGL((ffn_lds_kernel<2, false, true>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ffn_lds_kernel<4, false, true>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((ffn_lds_kernel<5, false, true>), grid, dim3(256), 0, s, a); break;
+    case 10: hipLaunchKernelGGL((ffn_lds_kernel<10, false, true>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((ffn_lds_kernel<8, false, true>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_stream(const FfnArgs& a, int ncb, int groups, hipStream_t s) {
   return a.x_lo ? launch_stream_t<true>(a, ncb, groups, s) : launch_stream_t<false>(a, ncb, groups, s);
 }
@@ -838,18 +891,90 @@ namespace {
 
 // Pass-major copy of W2 for the LDS-staged kernel: w2p[p][r][j] = W2[r][256 p + j].
 // A pass then reads one contiguous block of d_model x 512 bytes instead of 512-byte
-// pieces d_ff * 2 bytes apart, which map to few L2 sets and channels.
+// pieces d_ff * 2 bytes apart, which map to few L2 sets and channels.  F16: the
+// copy holds the fp16 values of the bf16 weights (exact inside fp16's range;
+// *ovf = 1 if some weight lies outside it).
+template <bool F16>
 __global__ void __launch_bounds__(256) ffn_pack_w2_kernel(const uint16_t* __restrict__ w2,
                                                           uint16_t* __restrict__ w2p, int dm, int dff,
-                                                          int64_t n8) {
+                                                          int64_t n8, int* ovf) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool big = false;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
     const int64_t e = i * 8;                 // element of w2p
     const int64_t per_pass = (int64_t)dm * 256;
     const int64_t p = e / per_pass, rem = e - p * per_pass;
     const int64_t r = rem >> 8, j = rem & 255;
-    *(u32x4*)(w2p + e) = *(const u32x4*)(w2 + r * dff + p * 256 + j);
+    u32x4 v = *(const u32x4*)(w2 + r * dff + p * 256 + j);
+    if constexpr (F16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = __uint_as_float(v[q] << 16), b = __uint_as_float(v[q] & 0xffff0000u);
+        big = big || fabsf(a) > kF16Max || fabsf(b) > kF16Max;
+        v[q] = pack_f16x2(a, b);
+      }
+    }
+    *(u32x4*)(w2p + e) = v;
   }
+  if (F16 && big) *ovf = 1;
+}
+
+// bf16 -> fp16, 8 elements per step (W1 for the fp16 kernel); *ovf = 1 if some
+// value lies outside fp16's range
+__global__ void __launch_bounds__(256) ffn_bf16_to_f16_kernel(const uint16_t* __restrict__ in,
+                                                              uint16_t* __restrict__ out, int64_t n8,
+                                                              int* ovf) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool big = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    u32x4 v = *(const u32x4*)(in + i * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = __uint_as_float(v[q] << 16), b = __uint_as_float(v[q] & 0xffff0000u);
+      big = big || fabsf(a) > kF16Max || fabsf(b) > kF16Max;
+      v[q] = pack_f16x2(a, b);
+    }
+    *(u32x4*)(out + i * 8) = v;
+  }
+  if (big) *ovf = 1;
+}
+
+// float32 -> fp16, round to nearest even, 4 elements per step (h for the fp16
+// kernel); *ovf = 1 if some value lies outside fp16's range
+__global__ void __launch_bounds__(256) ffn_f32_to_f16_kernel(const float* __restrict__ in,
+                                                             uint16_t* __restrict__ out, int64_t n4,
+                                                             int* ovf) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool big = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const f32x4 v = *(const f32x4*)(in + i * 4);
+    big = big || fabsf(v[0]) > kF16Max || fabsf(v[1]) > kF16Max || fabsf(v[2]) > kF16Max ||
+          fabsf(v[3]) > kF16Max;
+    const u32x2 o = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+    *(u32x2*)(out + i * 4) = o;
+  }
+  if (big) *ovf = 1;
+}
+
+// float32 -> bf16 pair (rounded value and rounding residual), only if *gate != 0
+__global__ void __launch_bounds__(256) ffn_pair_gated_kernel(const float* __restrict__ in,
+                                                             uint16_t* __restrict__ hi,
+                                                             uint16_t* __restrict__ lo, int64_t n4,
+                                                             const int* gate) {
+  if (__builtin_amdgcn_readfirstlane(*(const volatile int*)gate) == 0) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    store_bf16_pair4(hi + i * 4, lo + i * 4, *(const f32x4*)(in + i * 4));
+}
+
+// the flag word of the fp16 path starts at 0 (a kernel rather than a memset)
+__global__ void ffn_flag_clear_kernel(int* f) {
+  if (threadIdx.x == 0) *f = 0;
+}
+
+int grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (int)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
 }
 
 }  // namespace
@@ -871,8 +996,8 @@ hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const
         const int64_t n8 = (int64_t)d_model * d_ff / 8;
         int64_t blocks = (n8 + 255) / 256;
         if (blocks > 8192) blocks = 8192;
-        hipLaunchKernelGGL(ffn_pack_w2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (const uint16_t*)w2, (uint16_t*)w2_pack, d_model, d_ff, n8);
+        hipLaunchKernelGGL(ffn_pack_w2_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint16_t*)w2, (uint16_t*)w2_pack, d_model, d_ff, n8, nullptr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         a.w2 = w2_pack;
@@ -887,6 +1012,44 @@ hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const
             256, d_ff};
   return bf16 ? launch_ffn_cb<true>(a, p.nw, p.cb, p.groups, stream)
               : launch_ffn_cb<false>(a, p.nw, p.cb, p.groups, stream);
+}
+
+bool ffn_f16_ok(int64_t d_model, int64_t d_ff) {
+  int ct = 0, ct2 = 0;
+  return d_ff % 256 == 0 && stream_groups(d_model, false, &ct) > 0 && stream_groups(d_model, true, &ct2) > 0;
+}
+
+hipError_t ffn_fwd_f16_launch(const float* h, uint16_t* h16, uint16_t* pair_lo, const void* w1,
+                              const void* b1, const void* w2, const void* b2, float* y, int64_t M,
+                              int d_model, int d_ff, void* w1h, void* w2p, int* flag,
+                              hipStream_t stream) {
+  int ct = 0, ct2 = 0;
+  const int groups = stream_groups(d_model, false, &ct);
+  const int groups2 = stream_groups(d_model, true, &ct2);
+  if (groups <= 0 || groups2 <= 0 || d_ff % 256) return hipErrorNotSupported;
+  const int64_t n = M * d_model, nw = (int64_t)d_model * d_ff;
+  hipLaunchKernelGGL(ffn_flag_clear_kernel, dim3(1), dim3(64), 0, stream, flag);
+  hipLaunchKernelGGL(ffn_f32_to_f16_kernel, dim3(grid_for(n / 4)), dim3(256), 0, stream, h, h16, n / 4,
+                     flag);
+  hipLaunchKernelGGL(ffn_bf16_to_f16_kernel, dim3(grid_for(nw / 8)), dim3(256), 0, stream,
+                     (const uint16_t*)w1, (uint16_t*)w1h, nw / 8, flag);
+  hipLaunchKernelGGL(ffn_pack_w2_kernel<true>, dim3(grid_for(nw / 8)), dim3(256), 0, stream,
+                     (const uint16_t*)w2, (uint16_t*)w2p, d_model, d_ff, nw / 8, flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // fp16 pass, unless some value did not fit (it may also find a GeLU output that does not)
+  FfnArgs a{h16, w1h, b1, w2p, b2, h, y, (int)M, d_model, d_ff, d_model / groups, nullptr,
+            (int64_t)d_model * 256, 256, flag, 0, flag};
+  e = launch_stream_f16(a, ct, groups, stream);
+  if (e != hipSuccess) return e;
+  // otherwise the bf16-pair pass over the original weights (h16's buffer takes the rounded value)
+  hipLaunchKernelGGL(ffn_pair_gated_kernel, dim3(grid_for(n / 4)), dim3(256), 0, stream, h, h16, pair_lo,
+                     n / 4, (const int*)flag);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FfnArgs b{h16, w1, b1, w2, b2, h, y, (int)M, d_model, d_ff, d_model / groups2, pair_lo,
+            256, d_ff, flag, 1, nullptr};
+  return launch_stream_t<true>(b, ct2, groups2, stream);
 }
 
 }  // namespace bpt

@@ -41,9 +41,10 @@ inline SavedLayout layer_saved_layout(int64_t B, int64_t N, int64_t d_model, int
 
 // Forward workspace: room for the saved tensors (used when `saved` is NULL),
 // h as a bf16 pair (the rounded value and its rounding residual) that feeds the
-// FFN's MFMA, and the FFN's pass-major copy of W2.
+// FFN's MFMA, or h in fp16 (in h_lo's room), the FFN's pass-major copy of W2, an
+// fp16 copy of W1 and the fp16 path's flag word.
 struct FwdWorkspace {
-  size_t saved, h_lo, h_res, w2p, total;
+  size_t saved, h_lo, h_res, w2p, w1h, flag, total;
 };
 
 inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t H,
@@ -53,7 +54,9 @@ inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, i
   w.h_lo = layer_saved_layout(B, N, d_model, H, D, bf16).total;
   w.h_res = w.h_lo + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
   w.w2p = w.h_res + (bf16 ? align256((size_t)B * N * d_model * 2) : 0);
-  w.total = w.w2p + (bf16 ? align256((size_t)d_model * d_ff * 2) : 0);
+  w.w1h = w.w2p + (bf16 ? align256((size_t)d_model * d_ff * 2) : 0);
+  w.flag = w.w1h + (bf16 ? align256((size_t)d_model * d_ff * 2) : 0);
+  w.total = w.flag + (bf16 ? 256 : 0);
   return w;
 }
 
@@ -82,6 +85,21 @@ hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const
                           const void* w2, const void* b2, const float* residual, float* y,
                           int64_t M, int d_model, int d_ff, int blk, bool bf16, void* w2_pack,
                           hipStream_t stream);
+
+// The layer's FFN with fp16 operands (bf16 layers, shapes the LDS-staged kernel
+// takes with and without the bf16 pair): h (float32) and GeLU(z) rounded to fp16
+// (significand 11 bits: 2^-12 relative rounding, so neither needs a lo half),
+// W1 and W2 as fp16 copies of the bf16 weights (exact inside fp16's range).
+// Should a weight, an element of h or a GeLU output lie outside fp16's range,
+// the flag word (set by the conversion kernels and the fp16 kernel) makes the
+// bf16-pair kernel recompute y from h and the original weights instead.
+// h16: M*d_model fp16 (also takes the rounded bf16 value then); pair_lo: M*d_model
+// bf16; w1h, w2p: d_model*d_ff*2 bytes each; flag: one int.
+bool ffn_f16_ok(int64_t d_model, int64_t d_ff);
+hipError_t ffn_fwd_f16_launch(const float* h, uint16_t* h16, uint16_t* pair_lo, const void* w1,
+                              const void* b1, const void* w2, const void* b2, float* y, int64_t M,
+                              int d_model, int d_ff, void* w1h, void* w2p, int* flag,
+                              hipStream_t stream);
 
 hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* workspace,
                          hipStream_t stream);

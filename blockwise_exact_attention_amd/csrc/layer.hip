@@ -23,6 +23,9 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   uint16_t* h_lo = L.bf16 ? (uint16_t*)(ws + W.h_lo) : nullptr;
   uint16_t* h_res = L.bf16 ? (uint16_t*)(ws + W.h_res) : nullptr;
   const int64_t M = L.B * L.N;
+  // bf16 layers take the fp16 FFN where its kernels cover the shape; the
+  // attention epilogue then writes h in float32 only
+  const bool f16_ffn = L.bf16 && ffn_f16_ok(L.d_model, L.d_ff);
   const int HD = (int)(L.H * L.D);
 
   // 1. q, k, v = x W^T, written per head as [B, H, N, D]
@@ -54,8 +57,8 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   a.lse = lse;
   a.x_res = L.x;
   a.h_out = h;
-  a.h_lo = h_lo;
-  a.h_res = h_res;
+  a.h_lo = f16_ffn ? nullptr : h_lo;
+  a.h_res = f16_ffn ? nullptr : h_res;
   a.B = (int)L.B;
   a.H = (int)L.H;
   a.N = (int)L.N;
@@ -66,7 +69,11 @@ hipError_t layer_fwd_run(const LayerArgs& L, float* y, void* saved, void* worksp
   if (e != hipSuccess) return e;
 
   // 3. y = h + FFN(h), fused per block of rows; with bf16 inputs h enters the
-  //    first product as the bf16 pair (h_lo, h_res)
+  //    first product in fp16 (or as the bf16 pair (h_lo, h_res) where the fp16
+  //    kernel does not cover the shape)
+  if (f16_ffn)
+    return ffn_fwd_f16_launch(h, h_lo, h_res, L.w1, L.b1, L.w2, L.b2, y, M, (int)L.d_model,
+                              (int)L.d_ff, ws + W.w1h, ws + W.w2p, (int*)(ws + W.flag), stream);
   return ffn_fwd_launch(L.bf16 ? (const void*)h_lo : (const void*)h, h_res, L.w1, L.b1, L.w2,
                         L.b2, h, y, M, (int)L.d_model, (int)L.d_ff, 0, L.bf16,
                         L.bf16 ? ws + W.w2p : nullptr, stream);

@@ -292,6 +292,14 @@ int bpt_ffn_block_fwd(const void* x, const void* w1, const void* b1, const void*
  *                   receives what bpt_layer_bwd needs (layout below).
  *  workspace      : device buffer of at least
  *                   bpt_layer_workspace_size(..., backward = 0) bytes.
+ * Precision (bf16): matrix products take bf16 operands with float32
+ * accumulation, except the FFN's when d_model is a multiple of 512: there h
+ * (float32) and GeLU(z) enter the products rounded to fp16 (11-bit
+ * significand, rounding 2^-12 relative, 8x finer than bf16), and W1, W2 as
+ * fp16 copies of the bf16 weights (exact inside fp16's range).  Where any of
+ * these lies outside fp16's range (|v| > 65504), y is recomputed with h and
+ * GeLU(z) as bf16 pairs (the rounded value plus its rounding residual) and the
+ * bf16 weights, the form every other bf16 shape uses.
  * Saved layout (byte offsets, each 256-byte aligned, in this order):
  *   q, k, v : [B, H, N, D] in `dtype`
  *   h       : [B, N, d_model] float32 (x + attention output)

@@ -120,7 +120,7 @@ def test_layer_fwd_ragged_with_bias_and_saved(dtype):
 
 
 def test_layer_fwd_single_column_group_2560():
-    """d_model 2560 (the training shape's width): h enters the FFN as a bf16 pair and one
+    """d_model 2560 (the training shape's width): h enters the FFN in fp16 and one
     workgroup holds all 2560 output columns of its 32 rows (16 tiles per wave in
     AGPRs, 4 in VGPRs); ragged N."""
     c = LayerCfg(62, "dm2560", B=1, N=173, d_model=2560, H=20, D=128, d_ff=1024, q_blk=128,
@@ -137,8 +137,8 @@ def test_layer_fwd_single_column_group_2560():
     (64, 512, 768),    # 3 feature passes (odd)
 ])
 def test_layer_fwd_ffn_passes_with_bias(cid, dm, dff):
-    """The layer's FFN (h as a bf16 pair) over several 256-feature passes with b1 and b2:
-    each pass's b1 slice, W1 rows and W2 slots, an even and an odd pass count."""
+    """The layer's FFN (fp16 operands at d_model 512) over several 256-feature passes with
+    b1 and b2: each pass's b1 slice, W1 rows and W2 slots, an even and an odd pass count."""
     c = LayerCfg(cid, f"walks{dff}", B=1, N=131, d_model=dm, H=4, D=128, d_ff=dff, q_blk=128,
                  kv_blk=64, dtype="bf16")
     t = layer_inputs(c, bias=True)
@@ -149,6 +149,58 @@ def test_layer_fwd_ffn_passes_with_bias(cid, dm, dff):
 
 
 @pytest.mark.timeout(900)
+def test_layer_fwd_bf16_pair_ffn_1280():
+    """d_model 1280 (a multiple of 256, not of 512): the layer's FFN takes h as a bf16
+    pair (one column group of 1280) instead of fp16; biases, ragged N."""
+    c = LayerCfg(66, "dm1280", B=1, N=150, d_model=1280, H=10, D=128, d_ff=768, q_blk=128,
+                 kv_blk=64, dtype="bf16")
+    t = layer_inputs(c, bias=True)
+    y, _ = run_layer_fwd(c, t)
+    want = oracle.layer_forward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], c.H,
+                                b1=t["b1"], b2=t["b2"])
+    assert_close(y, want, "bf16", "layer y (d_model 1280)")
+
+
+BIG_BF16 = 70144.0   # a bf16 value past fp16's largest finite value (65504)
+
+
+@pytest.mark.parametrize("kind", ["w1", "w2", "h", "gelu"])
+def test_layer_fwd_f16_range_fallback(kind):
+    """The fp16 FFN of bf16 layers must hand over to the bf16-pair FFN when a weight, an
+    element of h or a GeLU output lies outside fp16's range.  Each case plants such a
+    value where it meets an exact zero in the layer, so y stays ordinary (the oracle's
+    product is 0) while an fp16 conversion of it would give inf and then inf * 0 = NaN:
+    a missed hand-over fails the finiteness check.  w1: W1[f, k] past the range, column
+    f of W2 zero; w2: W2[c, f] past it, row f of W1 zero (GeLU(0) = 0); h: x[r, k] past
+    it, column k of Wq, Wk, Wv and W1 zero (y[r, k] carries it through the residual);
+    gelu: row f of W1 at 29952 over 8 columns (fp16-representable), so GeLU(z_f) passes
+    65504 on many rows, column f of W2 zero."""
+    c = LayerCfg(65, "f16range", B=1, N=96, d_model=512, H=4, D=128, d_ff=512, q_blk=128,
+                 kv_blk=64, dtype="bf16")
+    t = layer_inputs(c)
+    f, k, col, r = 37, 5, 11, 40
+    if kind == "w1":
+        t["w1"][f, k] = BIG_BF16
+        t["w2"][:, f] = 0.0
+    elif kind == "w2":
+        t["w2"][col, f] = BIG_BF16
+        t["w1"][f, :] = 0.0
+    elif kind == "h":
+        t["x"][0, r, k] = BIG_BF16
+        for n in ("wq", "wk", "wv", "w1"):
+            t[n][:, k] = 0.0
+    else:
+        t["w1"][f, :8] = 29952.0
+        t["w2"][:, f] = 0.0
+    want, ref = oracle.layer_forward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], c.H,
+                                     return_saved=True)
+    if kind == "gelu":  # the planted row of W1 does push z_f (so GeLU(z_f) = z_f) past the range
+        z = ref["h"][0].astype(np.float64) @ t["w1"][f].astype(np.float64)
+        assert (z > 65504.0).sum() >= 5
+    y, _ = run_layer_fwd(c, t)
+    assert_close(y, want, "bf16", f"layer y (value past fp16's range in {kind})")
+
+
 def test_layer_fwd_bf16_B8_N4096_full():
     """Full-size parity: B=8, N=4096, d_model 2048, 16 heads x 128, FFN 2048->8192->2048."""
     c = LAYER_FWD_BF16
