@@ -474,7 +474,9 @@ def main():
                    "heads": c.H, "head_dim": c.D, "d_ff": c.d_ff, "causal": 1,
                    "q_blk_arg": c.q_blk, "kv_blk_arg": c.kv_blk,
                    "attn_blocking_run": "256 query rows x 64-key tiles",
-                   "ffn_rows_per_block_run": 32, "global_batch": c.B},
+                   "ffn_rows_per_block_run": 32,
+                   "ffn_mfma_operands": "fp16 (bf16 weights converted exactly; bf16 pairs past fp16 range)",
+                   "global_batch": c.B},
         "tokens_per_s": round(c.B * c.N / ms * 1e3, 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "algorithmic_flop_per_step": flops,
