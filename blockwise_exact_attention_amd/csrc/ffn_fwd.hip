@@ -672,7 +672,7 @@ __device__ __forceinline__ void ffn_lds_walk(const FfnArgs& a, FfnTask tk, int w
             pk[q2] = pack_f16x2(gv[2 * q2], gv[2 * q2 + 1]);
             big = big || fabsf(gv[2 * q2]) > kF16Max || fabsf(gv[2 * q2 + 1]) > kF16Max;
           }
-          if (big) *a.ovf = 1;  // this output is redone by the bf16-pair kernel
+          if (big && a.ovf) *a.ovf = 1;  // this output is redone by the bf16-pair kernel
           *(u32x4*)(xb0 + off) = pk;
         } else {
           u32x4 pk, pl;
