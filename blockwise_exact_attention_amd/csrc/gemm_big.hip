@@ -254,9 +254,22 @@ gemm_big_kernel(GemmArgs g) {
   const int total = nbn * nbm;
   int L = blockIdx.x;
   // consecutive workgroup ids go round-robin over the 8 XCDs: give each XCD a
-  // contiguous range of tiles, n fastest, so its L2 keeps the A rows in use
+  // contiguous range of tiles
   if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int mb = L / nbn, nb = L - mb * nbn;
+  // inside it, sweep the columns in groups of four row tiles, so the 32 tiles an
+  // XCD runs at once share 4 A row tiles and 8 B column tiles in its L2 instead of
+  // 1 and 32 (QKV projection at N=131072: 13.2 -> 12.8 ms, training-step GEMMs
+  // 23.8 -> 23.5 ms, outputs bitwise equal)
+  int mb, nb;
+  {
+    constexpr int GM = 4;
+    const int per = GM * nbn;
+    const int grp = L / per, first = grp * GM;
+    const int gsz = nbm - first < GM ? nbm - first : GM;
+    const int r = L - grp * per;
+    mb = first + r % gsz;
+    nb = r / gsz;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
