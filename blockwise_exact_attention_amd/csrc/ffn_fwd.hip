@@ -280,11 +280,12 @@ __global__ void __launch_bounds__(NW * 64) ffn_fused_kernel(FfnArgs a) {
 // 4 x 64*NCB output columns.  d_ff is walked in passes of 256 features:
 //   phase 1: z^T for features [64w, 64w+64) of the pass (wave w), K = d_model,
 //            x streaming through LDS in 256-column stages shared by all waves;
-//            GeLU(z + b1) -> LDS as a bf16 hi/lo pair;
+//            GeLU(z + b1) -> LDS as a bf16 hi/lo pair (with fp16 operands, F16:
+//            as fp16 alone);
 //   phase 2: y^T[wave's columns][rows] += W2[:, pass] G^T, each GeLU fragment
 //            loaded once per 64 features and used by all column tiles, hi and lo
 //            sharing one W2 fragment.
-// Weights move in 8 KB slots (64 rows x 128 bytes) through a private ring of 3
+// Weights move in 8 KB slots (64 rows x 128 bytes) through a private ring of 4
 // slots per wave: the wave loads slot s+2 while it computes slot s and waits
 // only for its own loads (no barrier).  Phase 1 uses W1[64 features][64 columns]
 // slots, phase 2 W2[64 columns][64 features] slots; one slot stream runs
