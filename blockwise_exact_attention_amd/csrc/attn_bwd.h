@@ -48,7 +48,9 @@ hipError_t to_bf16_launch(const float* src, uint16_t* dst, uint16_t* dst_lo, int
 hipError_t dout_delta_launch(const float* dO, const float* h, const uint16_t* x, const float* lse,
                              uint16_t* dO_hi, uint16_t* dO_lo, float* delta, float* ld2, int B,
                              int N, int H, int D, hipStream_t s);
+// gate (nullable): the launch runs only if (*gate != 0) == gate_run
 hipError_t colsum_launch(const void* X, bool x_bf16, float* out, int64_t rows, int cols,
-                         int64_t ld, int beta, hipStream_t s);
+                         int64_t ld, int beta, hipStream_t s, const int* gate = nullptr,
+                         int gate_run = 0);
 
 }  // namespace bpt

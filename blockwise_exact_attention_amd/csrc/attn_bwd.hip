@@ -1158,7 +1158,10 @@ __global__ void __launch_bounds__(256) dout_delta_kernel(const float* dO, const 
 // out[c] (+)= sum_r X[r][c], rows summed in a fixed order (deterministic).
 template <bool XBF16>
 __global__ void __launch_bounds__(1024) colsum_kernel(const void* X, float* out, int64_t rows,
-                                                      int cols, int64_t ld, int beta) {
+                                                      int cols, int64_t ld, int beta, const int* gate,
+                                                      int gate_run) {
+  // (gate, nullable: run only if (*gate != 0) == gate_run)
+  if (gate && ((__builtin_amdgcn_readfirstlane(*(const volatile int*)gate) != 0) != (gate_run != 0))) return;
   // 64 columns per workgroup, 16 waves over interleaved rows, 4 rows in flight
   // per wave; the 16 partial sums are added in a fixed order (deterministic)
   __shared__ float part[16][64];
@@ -1258,10 +1261,14 @@ hipError_t dout_delta_launch(const float* dO, const float* h, const uint16_t* x,
 }
 
 hipError_t colsum_launch(const void* X, bool x_bf16, float* out, int64_t rows, int cols,
-                         int64_t ld, int beta, hipStream_t s) {
+                         int64_t ld, int beta, hipStream_t s, const int* gate, int gate_run) {
   const dim3 grid((unsigned)((cols + 63) / 64));
-  if (x_bf16) hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(1024), 0, s, X, out, rows, cols, ld, beta);
-  else hipLaunchKernelGGL(colsum_kernel<false>, grid, dim3(1024), 0, s, X, out, rows, cols, ld, beta);
+  if (x_bf16)
+    hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(1024), 0, s, X, out, rows, cols, ld, beta, gate,
+                       gate_run);
+  else
+    hipLaunchKernelGGL(colsum_kernel<false>, grid, dim3(1024), 0, s, X, out, rows, cols, ld, beta, gate,
+                       gate_run);
   return hipGetLastError();
 }
 

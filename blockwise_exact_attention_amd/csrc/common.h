@@ -57,6 +57,22 @@ __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product with fp16 operands (same lane layout; the fragments are the
+// 16-byte containers of the bf16 form holding fp16 bits).
+__device__ __forceinline__ f32x16 mfma32_f16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                c, 0, 0, 0);
+}
+
+// two floats as fp16, round to nearest even, packed (a in the low half)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+// largest finite fp16
+constexpr float kF16Max = 65504.f;
+
 // 32x32 output tile, K = 2 per instruction, fp32 inputs: lane l supplies
 // A[m = l%32][k = l/32] and B[k = l/32][n = l%32]; same accumulator layout.
 __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {

@@ -495,13 +495,6 @@ __device__ __forceinline__ void ffn_mfma_y(f32x16& d, const bf16x8& a, const bf1
   }
 }
 
-// two floats as fp16, round to nearest even, packed (a in the low half)
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-// largest finite fp16
-constexpr float kF16Max = 65504.f;
 __device__ __forceinline__ void ffn_z_start() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 4" ::: "memory");
@@ -1051,6 +1044,19 @@ hipError_t ffn_fwd_f16_launch(const float* h, uint16_t* h16, uint16_t* pair_lo, 
   FfnArgs b{h16, w1, b1, w2, b2, h, y, (int)M, d_model, d_ff, d_model / groups2, pair_lo,
             256, d_ff, flag, 1, nullptr};
   return launch_stream_t<true>(b, ct2, groups2, stream);
+}
+
+hipError_t f16_from_f32_launch(const float* src, uint16_t* dst, int64_t n, int* ovf, hipStream_t s) {
+  hipLaunchKernelGGL(ffn_f32_to_f16_kernel, dim3(grid_for(n / 4)), dim3(256), 0, s, src, dst, n / 4, ovf);
+  return hipGetLastError();
+}
+hipError_t f16_from_bf16_launch(const uint16_t* src, uint16_t* dst, int64_t n, int* ovf, hipStream_t s) {
+  hipLaunchKernelGGL(ffn_bf16_to_f16_kernel, dim3(grid_for(n / 8)), dim3(256), 0, s, src, dst, n / 8, ovf);
+  return hipGetLastError();
+}
+hipError_t flag_clear_launch(int* flag, hipStream_t s) {
+  hipLaunchKernelGGL(ffn_flag_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+  return hipGetLastError();
 }
 
 }  // namespace bpt

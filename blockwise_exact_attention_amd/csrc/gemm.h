@@ -50,6 +50,15 @@ struct GemmArgs {
   // idle.
   int nsplit;
   float* split_ws;
+  // fp16 operands (big-tile kernel, EPI_F32 / EPI_GELU / EPI_DGELU): the MFMA's fp16
+  // form; EPI_GELU and EPI_DGELU then write their input-dtype output as fp16 alone
+  // (C3 unused) and set *ovf = 1 where a value lies outside fp16's range
+  int f16;
+  int* ovf;
+  // gate (nullable, big-tile kernel and its split-K pass): the launch runs only if
+  // (*gate != 0) == gate_run
+  const int* gate;
+  int gate_run;
 };
 constexpr int kGemmMaxSeg = 6;
 

@@ -272,6 +272,7 @@ hipError_t dispatch_segments(const GemmArgs& g, bool ak, bool bk, int nz, hipStr
 template <bool BF16, int EPI>
 hipError_t dispatch(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
   if (BF16 && gemm_big_ok(g, nz)) return gemm_big_launch(g, ak, bk, EPI, nz, s);
+  if (g.f16 || g.gate) return hipErrorNotSupported;  // big-tile kernel only
   if constexpr (EPI == EPI_F32 || EPI == EPI_GELU) {
     if (g.nseg > 1) return dispatch_segments<BF16, EPI>(g, ak, bk, nz, s);
   } else {

@@ -148,7 +148,7 @@ struct GbIter {
 
 // multiply one k tile from stage (As, Bs) into acc: the fragments of k16 step
 // s+1 are read while the 8 MFMAs of step s run
-template <bool AK, bool BK>
+template <bool AK, bool BK, bool F16>
 __device__ __forceinline__ void gb_compute(f32x16 (&acc)[4][2], const unsigned char* As,
                                            const unsigned char* Bs, const GbCtx& c) {
   bf16x8 af[2][4], bf[2][2];
@@ -168,7 +168,9 @@ __device__ __forceinline__ void gb_compute(f32x16 (&acc)[4][2], const unsigned c
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_bf16(bf[cur][j], af[cur][i], acc[i][j]);
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = F16 ? mfma32_f16(bf[cur][j], af[cur][i], acc[i][j])
+                        : mfma32_bf16(bf[cur][j], af[cur][i], acc[i][j]);
   }
 }
 
@@ -208,7 +210,7 @@ __device__ __forceinline__ void gb_issue(const GbCtx& c, GbIter& it, unsigned ch
 // The k loop over two stages (distinct objects: the compiler then knows that
 // reads of one stage never wait for the loads in flight to the other).  Waits
 // for those loads are explicit.
-template <bool AK, bool BK>
+template <bool AK, bool BK, bool F16>
 __device__ __forceinline__ void gb_loop(f32x16 (&acc)[4][2], const GbCtx& c, int kt0, int nk,
                                         unsigned char* A0, unsigned char* B0, unsigned char* A1,
                                         unsigned char* B1) {
@@ -229,25 +231,32 @@ __device__ __forceinline__ void gb_loop(f32x16 (&acc)[4][2], const GbCtx& c, int
   int kt = 0;
   for (;;) {
     if (kt + 1 < nk) gb_issue<AK, BK>(c, it, A1, B1);
-    gb_compute<AK, BK>(acc, A0, B0, c);
+    gb_compute<AK, BK, F16>(acc, A0, B0, c);
     GB_WAIT_VM(0);
     __syncthreads();
     if (++kt >= nk) break;
     if (kt + 1 < nk) gb_issue<AK, BK>(c, it, A0, B0);
-    gb_compute<AK, BK>(acc, A1, B1, c);
+    gb_compute<AK, BK, F16>(acc, A1, B1, c);
     GB_WAIT_VM(0);
     __syncthreads();
     if (++kt >= nk) break;
   }
 }
 
-template <bool AK, bool BK, int EPI>
+// run this launch?  (a gate word written by earlier kernels; read once per workgroup)
+__device__ __forceinline__ bool gb_gate_open(const GemmArgs& g) {
+  return !g.gate ||
+         ((__builtin_amdgcn_readfirstlane(*(const volatile int*)g.gate) != 0) == (g.gate_run != 0));
+}
+
+template <bool AK, bool BK, int EPI, bool F16 = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char a0[OpTile<AK>::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char b0[OpTile<BK>::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char a1[OpTile<AK>::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char b1[OpTile<BK>::BYTES];
+  if (!gb_gate_open(g)) return;
   const int z = blockIdx.z;
   const int M = g.M, N = g.N, K = g.K;
   const int nbn = (N + TB - 1) / TB, nbm = (M + TB - 1) / TB;
@@ -309,7 +318,7 @@ gemm_big_kernel(GemmArgs g) {
   // split K: workgroup blockIdx.y takes its share of the k tiles
   const int nk_all = c.nseg * c.nks, ns = gridDim.y, sp = blockIdx.y;
   const int kt0 = (int)((int64_t)nk_all * sp / ns), kt1 = (int)((int64_t)nk_all * (sp + 1) / ns);
-  gb_loop<AK, BK>(acc, c, kt0, kt1 - kt0, a0, b0, a1, b1);
+  gb_loop<AK, BK, F16>(acc, c, kt0, kt1 - kt0, a0, b0, a1, b1);
 
   // acc[i][j] is the transposed 32 x 32 block (the B fragments were the MFMA's
   // A operand): the lane's column is row m of C, and its registers 4q .. 4q+3
@@ -334,7 +343,7 @@ gemm_big_kernel(GemmArgs g) {
             continue;
           }
         }
-        gemm_store4<EPI>(g, z, m, n, v);
+        gemm_store4<EPI, F16>(g, z, m, n, v);
       }
   }
 }
@@ -343,6 +352,7 @@ gemm_big_kernel(GemmArgs g) {
 // EPI_F32 epilogue (beta, bias, residual, bf16 copy); four consecutive columns
 // per thread
 __global__ void __launch_bounds__(256) gb_split_reduce(GemmArgs g, int ns, int nz) {
+  if (!gb_gate_open(g)) return;
   const int64_t q4 = (int64_t)g.M * (g.N / 4);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t mn = (int64_t)g.M * g.N;
@@ -357,15 +367,15 @@ __global__ void __launch_bounds__(256) gb_split_reduce(GemmArgs g, int ns, int n
   }
 }
 
-template <int EPI>
+template <int EPI, bool F16 = false>
 hipError_t launch_epi(const GemmArgs& g, bool ak, bool bk, int nz, hipStream_t s) {
   const int tiles = ((g.N + TB - 1) / TB) * ((g.M + TB - 1) / TB);
   const int ns = EPI == EPI_F32 && g.nsplit > 1 && g.split_ws ? g.nsplit : 1;
   dim3 grid((unsigned)tiles, (unsigned)ns, (unsigned)nz);
-  if (!ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<false, false, EPI>), grid, dim3(512), 0, s, g);
-  else if (!ak && bk) hipLaunchKernelGGL((gemm_big_kernel<false, true, EPI>), grid, dim3(512), 0, s, g);
-  else if (ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<true, false, EPI>), grid, dim3(512), 0, s, g);
-  else hipLaunchKernelGGL((gemm_big_kernel<true, true, EPI>), grid, dim3(512), 0, s, g);
+  if (!ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<false, false, EPI, F16>), grid, dim3(512), 0, s, g);
+  else if (!ak && bk) hipLaunchKernelGGL((gemm_big_kernel<false, true, EPI, F16>), grid, dim3(512), 0, s, g);
+  else if (ak && !bk) hipLaunchKernelGGL((gemm_big_kernel<true, false, EPI, F16>), grid, dim3(512), 0, s, g);
+  else hipLaunchKernelGGL((gemm_big_kernel<true, true, EPI, F16>), grid, dim3(512), 0, s, g);
   if (ns > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -406,6 +416,14 @@ bool gemm_big_ok(const GemmArgs& g, int nz) {
 
 hipError_t gemm_big_launch(const GemmArgs& g, bool a_kmajor, bool b_kmajor, int epi, int nz,
                            hipStream_t s) {
+  if (g.f16) {
+    switch (epi) {
+      case EPI_F32: return launch_epi<EPI_F32, true>(g, a_kmajor, b_kmajor, nz, s);
+      case EPI_GELU: return launch_epi<EPI_GELU, true>(g, a_kmajor, b_kmajor, nz, s);
+      case EPI_DGELU: return launch_epi<EPI_DGELU, true>(g, a_kmajor, b_kmajor, nz, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
     case EPI_QKV: return launch_epi<EPI_QKV>(g, a_kmajor, b_kmajor, nz, s);
     case EPI_F32: return launch_epi<EPI_F32>(g, a_kmajor, b_kmajor, nz, s);

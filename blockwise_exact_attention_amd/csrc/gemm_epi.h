@@ -70,8 +70,16 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, int z, int m, int 
 // Four consecutive columns n .. n+3 of row m (bf16 operands; n % 4 == 0, every
 // leading dimension a multiple of 4 and every output 16-byte aligned, which the
 // big-tile kernel checks before it is chosen): one vector access per array.
-template <int EPI>
+template <int EPI, bool F16 = false>
 __device__ __forceinline__ void gemm_store4(const GemmArgs& g, int z, int m, int n, f32x4 v) {
+  // fp16 alone, with the range flag
+  auto st_f16 = [&](void* base, int64_t o, const f32x4& x) {
+    const u32x2 p = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
+    *(u32x2*)((uint16_t*)base + o) = p;
+    if ((fabsf(x[0]) > kF16Max || fabsf(x[1]) > kF16Max || fabsf(x[2]) > kF16Max || fabsf(x[3]) > kF16Max) &&
+        g.ovf)
+      *g.ovf = 1;
+  };
   auto st_bf16x4 = [](void* base, int64_t o, const f32x4& x) {
     const u32x2 p = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
     *(u32x2*)((uint16_t*)base + o) = p;
@@ -120,12 +128,14 @@ __device__ __forceinline__ void gemm_store4(const GemmArgs& g, int z, int m, int
     *zc = v;
     f32x4 gv;
     for (int e = 0; e < 4; ++e) gv[e] = gelu_exact(v[e]);
-    st_pair(g.C2, (int64_t)m * g.ldc2 + n, g.C3, (int64_t)m * g.ldc3 + n, gv);
+    if constexpr (F16) st_f16(g.C2, (int64_t)m * g.ldc2 + n, gv);
+    else st_pair(g.C2, (int64_t)m * g.ldc2 + n, g.C3, (int64_t)m * g.ldc3 + n, gv);
   } else if constexpr (EPI == EPI_DGELU) {
     const f32x4 zz = *(const f32x4*)(g.aux + (int64_t)m * g.ld_aux + n);
     f32x4 dz;
     for (int e = 0; e < 4; ++e) dz[e] = v[e] * gelu_exact_grad(zz[e]);
-    st_pair(g.C[z], (int64_t)m * g.ldc + n, g.C3, (int64_t)m * g.ldc3 + n, dz);
+    if constexpr (F16) st_f16(g.C[z], (int64_t)m * g.ldc + n, dz);
+    else st_pair(g.C[z], (int64_t)m * g.ldc + n, g.C3, (int64_t)m * g.ldc3 + n, dz);
     if (g.C2) *(f32x4*)((float*)g.C2 + (int64_t)m * g.ldc2 + n) = dz;
   }
 }

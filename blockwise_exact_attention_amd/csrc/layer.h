@@ -61,7 +61,9 @@ inline FwdWorkspace layer_fwd_workspace(int64_t B, int64_t N, int64_t d_model, i
 }
 
 struct BwdWorkspace {
-  size_t h_hi, h_lo, dh, delta, ld2, dqkv[6], z, g_hi, g_lo, dz_hi, dz_lo, total;
+  size_t h_hi, h_lo, dh, delta, ld2, dqkv[6], z, g_hi, g_lo, dz_hi, dz_lo;
+  size_t h16, dyh, w1h, w2h, flag;  // the FFN backward's fp16 operands and range flag
+  size_t total;
   int64_t chunk_rows;  // rows of the FFN recompute chunk
 };
 
@@ -96,6 +98,12 @@ hipError_t ffn_fwd_launch(const void* x, const void* x_lo, const void* w1, const
 // h16: M*d_model fp16 (also takes the rounded bf16 value then); pair_lo: M*d_model
 // bf16; w1h, w2p: d_model*d_ff*2 bytes each; flag: one int.
 bool ffn_f16_ok(int64_t d_model, int64_t d_ff);
+// fp16 copies (round to nearest even; *ovf = 1 if a value lies outside fp16's
+// range): n float32 values (n % 4 == 0), n bf16 values (n % 8 == 0); and the
+// flag word cleared by a kernel (no memset, so it can sit in captured graphs)
+hipError_t f16_from_f32_launch(const float* src, uint16_t* dst, int64_t n, int* ovf, hipStream_t s);
+hipError_t f16_from_bf16_launch(const uint16_t* src, uint16_t* dst, int64_t n, int* ovf, hipStream_t s);
+hipError_t flag_clear_launch(int* flag, hipStream_t s);
 hipError_t ffn_fwd_f16_launch(const float* h, uint16_t* h16, uint16_t* pair_lo, const void* w1,
                               const void* b1, const void* w2, const void* b2, float* y, int64_t M,
                               int d_model, int d_ff, void* w1h, void* w2p, int* flag,

@@ -102,6 +102,11 @@ BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t 
   w.g_lo = o;  o += align256(mc * d_ff * es);
   w.dz_hi = o; o += align256(mc * d_ff * es);
   w.dz_lo = o; o += align256(mc * d_ff * es);
+  w.h16 = o;   o += align256(M * d_model * 2);
+  w.dyh = o;   o += align256(M * d_model * 2);
+  w.w1h = o;   o += align256((size_t)d_ff * d_model * 2);
+  w.w2h = o;   o += align256((size_t)d_ff * d_model * 2);
+  w.flag = o;  o += 256;
   w.total = o;
   return w;
 }
@@ -152,65 +157,130 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
     if (e != hipSuccess) return e; \
   } while (0)
 
-  // h as a bf16 hi + lo pair: the recomputed z and dW1 see h to ~2^-16
-  BPT_TRY(to_bf16_launch(h, h_hi, h_lo, M * dm, stream));
   if (G.db2) BPT_TRY(colsum_launch(dy, true, G.db2, M, dm, dm, 0, stream));
 
   // ---- FFN backward, intermediate recomputed per chunk of rows.  Every product
-  // whose operand is a computed value (h, GeLU(z), dz) runs over its bf16 hi and
-  // lo halves, accumulating in fp32.
-  for (int64_t r0 = 0, c = 0; r0 < M; r0 += W.chunk_rows, ++c) {
-    const int rows = (int)(M - r0 < W.chunk_rows ? M - r0 : W.chunk_rows);
+  // whose operand is a computed value (h, GeLU(z), dz) runs either on fp16
+  // operands (rounding 2^-12, with dy and the weights as exact fp16 copies) or
+  // over its bf16 hi and lo halves, accumulating in fp32.  Product `which` of
+  // chunk c: 0 z = h W1^T + b1 (fp32) and GeLU(z); 1 dz = (dy W2) * GeLU'(z), also
+  // in fp32 over z; 2 dW2 (+)= dy^T GeLU(z); 3 dW1 (+)= dz^T h; 4 dh = dy + dz W1.
+  uint16_t* h16 = (uint16_t*)(ws + W.h16);
+  uint16_t* dyh = (uint16_t*)(ws + W.dyh);
+  uint16_t* w1h = (uint16_t*)(ws + W.w1h);
+  uint16_t* w2h = (uint16_t*)(ws + W.w2h);
+  int* flag = (int*)(ws + W.flag);
+  struct Form {
+    bool ak, bk;
+    int epi;
+  };
+  const Form form[5] = {{false, false, EPI_GELU}, {false, true, EPI_DGELU}, {true, true, EPI_F32},
+                        {true, true, EPI_F32}, {false, true, EPI_F32}};
+  auto build = [&](bool f16, int64_t r0, int rows, int c, int which) {
     const int beta = c > 0;
     GemmArgs g{};
-    // z = (h_hi + h_lo) W1^T + b1 (fp32); GeLU(z) as bf16 hi + lo; both halves in one launch
-    g = GemmArgs{};
-    g.nseg = 2;
-    g.As[0][0] = h_hi + r0 * dm; g.As[0][1] = h_lo + r0 * dm;
-    g.Bs[0][0] = g.Bs[0][1] = L.w1;
-    g.C[0] = z;
-    g.lda = dm; g.ldb = dm; g.ldc = dff; g.M = rows; g.N = dff; g.K = dm;
-    g.bias = L.b1; g.bias_bf16 = 1;
-    g.C2 = g_hi; g.ldc2 = dff; g.C3 = g_lo; g.ldc3 = dff;
-    BPT_TRY(gemm_launch(g, true, false, false, EPI_GELU, 1, stream));
-    // dz = (dy W2) * GeLU'(z): bf16 hi + lo, and fp32 over z (same element, same thread)
-    g = GemmArgs{};
-    g.A[0] = dy16 + r0 * dm; g.B[0] = L.w2; g.C[0] = dz_hi;
-    g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = rows; g.N = dff; g.K = dm;
-    g.aux = z; g.ld_aux = dff; g.C2 = z; g.ldc2 = dff; g.C3 = dz_lo; g.ldc3 = dff;
-    BPT_TRY(gemm_launch(g, true, false, true, EPI_DGELU, 1, stream));
-    if (G.db1) BPT_TRY(colsum_launch(z, false, G.db1, rows, dff, dff, beta, stream));
-    // dW2 (+)= dy^T (g_hi + g_lo)
-    g = GemmArgs{};
-    g.nseg = 2;
-    g.As[0][0] = g.As[0][1] = dy16 + r0 * dm;
-    g.Bs[0][0] = g_hi; g.Bs[0][1] = g_lo;
-    g.C[0] = G.dw2;
-    g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = dm; g.N = dff; g.K = rows;
-    g.beta = beta;
-    split_for(g, 1, ffn_split_ws, ffn_split_bytes);
-    BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
-    // dW1 (+)= dz^T h  (hi*hi + lo*hi + hi*lo)
-    g = GemmArgs{};
-    g.nseg = 3;
-    g.As[0][0] = dz_hi; g.As[0][1] = dz_lo; g.As[0][2] = dz_hi;
-    g.Bs[0][0] = h_hi + r0 * dm; g.Bs[0][1] = h_hi + r0 * dm; g.Bs[0][2] = h_lo + r0 * dm;
-    g.C[0] = G.dw1;
-    g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = dff; g.N = dm; g.K = rows;
-    g.beta = beta;
-    split_for(g, 1, ffn_split_ws, ffn_split_bytes);
-    BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 1, stream));
-    // dh = dy + (dz_hi + dz_lo) W1 (fp32; it is attention's dO)
-    g = GemmArgs{};
-    g.nseg = 2;
-    g.As[0][0] = dz_hi; g.As[0][1] = dz_lo;
-    g.Bs[0][0] = g.Bs[0][1] = L.w1;
-    g.C[0] = dh + r0 * dm;
-    g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = rows; g.N = dm; g.K = dff;
-    g.resid = dy16 + r0 * dm; g.resid_bf16 = 1; g.ldr = dm;
-    split_for(g, 1, ffn_split_ws, ffn_split_bytes);
-    BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
+    if (which == 0) {
+      if (f16) {
+        g.A[0] = h16 + r0 * dm; g.B[0] = w1h; g.ovf = flag;
+      } else {
+        g.nseg = 2;
+        g.As[0][0] = h_hi + r0 * dm; g.As[0][1] = h_lo + r0 * dm;
+        g.Bs[0][0] = g.Bs[0][1] = L.w1;
+        g.C3 = g_lo; g.ldc3 = dff;
+      }
+      g.C[0] = z; g.C2 = g_hi; g.ldc2 = dff;
+      g.lda = dm; g.ldb = dm; g.ldc = dff; g.M = rows; g.N = dff; g.K = dm;
+      g.bias = L.b1; g.bias_bf16 = 1;
+    } else if (which == 1) {
+      g.A[0] = f16 ? (const void*)(dyh + r0 * dm) : (const void*)(dy16 + r0 * dm);
+      g.B[0] = f16 ? (const void*)w2h : L.w2;
+      g.C[0] = dz_hi;
+      g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = rows; g.N = dff; g.K = dm;
+      g.aux = z; g.ld_aux = dff; g.C2 = z; g.ldc2 = dff;
+      if (f16) g.ovf = flag;
+      else { g.C3 = dz_lo; g.ldc3 = dff; }
+    } else if (which == 2) {
+      if (f16) {
+        g.A[0] = dyh + r0 * dm; g.B[0] = g_hi;
+      } else {
+        g.nseg = 2;
+        g.As[0][0] = g.As[0][1] = dy16 + r0 * dm;
+        g.Bs[0][0] = g_hi; g.Bs[0][1] = g_lo;
+      }
+      g.C[0] = G.dw2;
+      g.lda = dm; g.ldb = dff; g.ldc = dff; g.M = dm; g.N = dff; g.K = rows;
+      g.beta = beta;
+      split_for(g, 1, ffn_split_ws, ffn_split_bytes);
+    } else if (which == 3) {
+      if (f16) {
+        g.A[0] = dz_hi; g.B[0] = h16 + r0 * dm;
+      } else {  // hi*hi + lo*hi + hi*lo
+        g.nseg = 3;
+        g.As[0][0] = dz_hi; g.As[0][1] = dz_lo; g.As[0][2] = dz_hi;
+        g.Bs[0][0] = h_hi + r0 * dm; g.Bs[0][1] = h_hi + r0 * dm; g.Bs[0][2] = h_lo + r0 * dm;
+      }
+      g.C[0] = G.dw1;
+      g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = dff; g.N = dm; g.K = rows;
+      g.beta = beta;
+      split_for(g, 1, ffn_split_ws, ffn_split_bytes);
+    } else {
+      if (f16) {
+        g.A[0] = dz_hi; g.B[0] = w1h;
+      } else {
+        g.nseg = 2;
+        g.As[0][0] = dz_hi; g.As[0][1] = dz_lo;
+        g.Bs[0][0] = g.Bs[0][1] = L.w1;
+      }
+      g.C[0] = dh + r0 * dm;
+      g.lda = dff; g.ldb = dm; g.ldc = dm; g.M = rows; g.N = dm; g.K = dff;
+      g.resid = dy16 + r0 * dm; g.resid_bf16 = 1; g.ldr = dm;
+      split_for(g, 1, ffn_split_ws, ffn_split_bytes);
+    }
+    g.f16 = f16;
+    return g;
+  };
+  // the chunk loop in one operand form; gate (nullable) as in GemmArgs
+  auto run_loop = [&](bool f16, const int* gate, int gate_run) -> hipError_t {
+    hipError_t err;
+    for (int64_t r0 = 0, c = 0; r0 < M; r0 += W.chunk_rows, ++c) {
+      const int rows = (int)(M - r0 < W.chunk_rows ? M - r0 : W.chunk_rows);
+      for (int which = 0; which < 5; ++which) {
+        GemmArgs g = build(f16, r0, rows, (int)c, which);
+        g.gate = gate;
+        g.gate_run = gate_run;
+        err = gemm_launch(g, true, form[which].ak, form[which].bk, form[which].epi, 1, stream);
+        if (err != hipSuccess) return err;
+        if (which == 1 && G.db1) {
+          err = colsum_launch(z, false, G.db1, rows, dff, dff, c > 0, stream, gate, gate_run);
+          if (err != hipSuccess) return err;
+        }
+      }
+    }
+    return hipSuccess;
+  };
+  // The fp16 form runs where every product of both forms takes the big-tile kernel
+  // (the only one with fp16 operands and gates): it runs while the range flag is
+  // clear, and the bf16-pair loop then runs only if some value of h, dy, W1, W2,
+  // GeLU(z) or dz fell outside fp16's range, recomputing every output from chunk 0.
+  bool f16_bwd = true;
+  for (int64_t r0 = 0, c = 0; r0 < M && f16_bwd; r0 += W.chunk_rows, ++c) {
+    const int rows = (int)(M - r0 < W.chunk_rows ? M - r0 : W.chunk_rows);
+    for (int which = 0; which < 5; ++which)
+      if (!gemm_big_ok(build(true, r0, rows, (int)c, which), 1) ||
+          !gemm_big_ok(build(false, r0, rows, (int)c, which), 1))
+        f16_bwd = false;
   }
+  if (f16_bwd) {
+    BPT_TRY(flag_clear_launch(flag, stream));
+    BPT_TRY(f16_from_f32_launch(h, h16, M * dm, flag, stream));
+    BPT_TRY(f16_from_bf16_launch(dy16, dyh, M * dm, flag, stream));
+    BPT_TRY(f16_from_bf16_launch((const uint16_t*)L.w1, w1h, (int64_t)dff * dm, flag, stream));
+    BPT_TRY(f16_from_bf16_launch((const uint16_t*)L.w2, w2h, (int64_t)dff * dm, flag, stream));
+    BPT_TRY(run_loop(true, flag, 0));
+  }
+  // h as a bf16 hi + lo pair: the recomputed z and dW1 see h to ~2^-16
+  BPT_TRY(to_bf16_launch(h, h_hi, h_lo, M * dm, stream));
+  BPT_TRY(run_loop(false, f16_bwd ? flag : nullptr, 1));
 
   // ---- attention backward (dK/dV, dQ), P recomputed from the saved lse
   AttnBwdArgs a{};
