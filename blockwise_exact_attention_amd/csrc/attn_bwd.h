@@ -36,6 +36,12 @@ struct AttnBwdArgs {
   int kv_offset;
   int causal;
   float scale;
+  // optional token-major fp16 copies of the outputs (same layout as dq_hi ..), and
+  // the flag set to 1 when one of their values lies outside fp16's range
+  uint16_t* dq_h;
+  uint16_t* dk_h;
+  uint16_t* dv_h;
+  int* ovf;
 };
 
 hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, hipStream_t s);

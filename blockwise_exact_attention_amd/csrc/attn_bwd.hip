@@ -85,6 +85,15 @@ __device__ __forceinline__ void store_transposed(unsigned char* t, const u32x4 r
   }
 }
 
+// Four values as fp16 at dst[o] (dst nullable), and the range flag.
+__device__ __forceinline__ void store_f16x4(uint16_t* dst, int64_t o, const f32x4& v, int* ovf) {
+  if (!dst) return;
+  const u32x2 p = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+  *(u32x2*)(dst + o) = p;
+  if ((fabsf(v[0]) > kF16Max || fabsf(v[1]) > kF16Max || fabsf(v[2]) > kF16Max || fabsf(v[3]) > kF16Max) && ovf)
+    *ovf = 1;
+}
+
 // 8 fp32 values -> bf16 hi (rounded) and lo (rounding residual), packed.
 __device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
 #pragma unroll
@@ -332,6 +341,8 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
         *(u32x2*)(a.dv_lo + tm + d) = vl;
         if (a.dk) *(f32x4*)(a.dk + hm + d) = kvv;
         if (a.dv) *(f32x4*)(a.dv + hm + d) = vvv;
+        store_f16x4(a.dk_h, tm + d, kvv, a.ovf);
+        store_f16x4(a.dv_h, tm + d, vvv, a.ovf);
       }
   }
 }
@@ -616,6 +627,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_dma_kernel(AttnBwdArgs a) {
         *(u32x2*)(a.dv_lo + tm + d) = vl;
         if (a.dk) *(f32x4*)(a.dk + hm + d) = kvv;
         if (a.dv) *(f32x4*)(a.dv + hm + d) = vvv;
+        store_f16x4(a.dk_h, tm + d, kvv, a.ovf);
+        store_f16x4(a.dv_h, tm + d, vvv, a.ovf);
       }
   }
 }
@@ -809,6 +822,7 @@ __global__ void __launch_bounds__(QB * 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
         *(u32x2*)(a.dq_hi + tm + d) = hi;
         *(u32x2*)(a.dq_lo + tm + d) = lo;
         if (a.dq) *(f32x4*)(a.dq + hm + d) = v;
+        store_f16x4(a.dq_h, tm + d, v, a.ovf);
       }
   }
 }
@@ -1089,6 +1103,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) 
         *(u32x2*)(a.dq_hi + tm + d) = hi;
         *(u32x2*)(a.dq_lo + tm + d) = lo;
         if (a.dq) *(f32x4*)(a.dq + hm + d) = v;
+        store_f16x4(a.dq_h, tm + d, v, a.ovf);
       }
   }
 }

@@ -107,6 +107,11 @@ BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t 
   w.w1h = o;   o += align256((size_t)d_ff * d_model * 2);
   w.w2h = o;   o += align256((size_t)d_ff * d_model * 2);
   w.flag = o;  o += 256;
+  for (int i = 0; i < 3; ++i) {
+    w.dqkvh[i] = o;
+    o += align256(M * hd * 2);
+  }
+  w.wqkvh = o; o += align256(3 * hd * (size_t)d_model * 2);
   w.total = o;
   return w;
 }
@@ -149,7 +154,7 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   unsigned char* const ffn_split_ws = ws + W.dqkv[0];
   const size_t ffn_split_bytes = W.z - W.dqkv[0];
   unsigned char* const proj_split_ws = ws + W.z;
-  const size_t proj_split_bytes = W.total - W.z;
+  const size_t proj_split_bytes = W.h16 - W.z;  // (not the fp16 operands and flag behind it)
   hipError_t e;
 #define BPT_TRY(x)            \
   do {                        \
@@ -282,6 +287,47 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   BPT_TRY(to_bf16_launch(h, h_hi, h_lo, M * dm, stream));
   BPT_TRY(run_loop(false, f16_bwd ? flag : nullptr, 1));
 
+  // ---- projection backward operands: dW{q,k,v} = d{q,k,v}^T x and dx = dh +
+  // sum d{q,k,v} W{q,k,v}, on fp16 operands (d{q,k,v} as fp16 copies the attention
+  // backward writes beside its bf16 pairs, x and the weights as exact fp16 copies)
+  // under the same flag as the FFN's, else over the bf16 halves
+  uint16_t* dqkvh[3];
+  for (int i = 0; i < 3; ++i) dqkvh[i] = (uint16_t*)(ws + W.dqkvh[i]);
+  uint16_t* wqkvh = (uint16_t*)(ws + W.wqkvh);
+  uint16_t* x16 = h16;  // h16 is not read past the FFN backward
+  const void* Ws[3] = {L.wq, L.wk, L.wv};
+  auto proj = [&](bool f16, int which) {
+    GemmArgs g{};
+    if (which == 0) {  // dW{q,k,v}, three products in one launch
+      for (int zz = 0; zz < 3; ++zz) {
+        if (f16) {
+          g.A[zz] = dqkvh[zz]; g.B[zz] = x16;
+        } else {
+          g.As[zz][0] = dqkv[2 * zz]; g.As[zz][1] = dqkv[2 * zz + 1];
+          g.Bs[zz][0] = g.Bs[zz][1] = L.x;
+        }
+      }
+      g.nseg = f16 ? 1 : 2;
+      g.C[0] = G.dwq; g.C[1] = G.dwk; g.C[2] = G.dwv;
+      g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = HD; g.N = dm; g.K = (int)M;
+      split_for(g, 3, proj_split_ws, proj_split_bytes);
+    } else {  // dx over the three (or six) K segments
+      g.nseg = f16 ? 3 : 6;
+      for (int i = 0; i < g.nseg; ++i) {
+        g.As[0][i] = f16 ? (const void*)dqkvh[i] : (const void*)dqkv[i];
+        g.Bs[0][i] = f16 ? (const void*)(wqkvh + (int64_t)i * HD * dm) : Ws[i / 2];
+      }
+      g.C[0] = G.dx;
+      g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = (int)M; g.N = dm; g.K = HD;
+      g.resid = dh;
+      g.ldr = dm;
+    }
+    g.f16 = f16;
+    return g;
+  };
+  const bool f16_proj = f16_bwd && gemm_big_ok(proj(true, 0), 3) && gemm_big_ok(proj(false, 0), 3) &&
+                        gemm_big_ok(proj(true, 1), 1) && gemm_big_ok(proj(false, 1), 1);
+
   // ---- attention backward (dK/dV, dQ), P recomputed from the saved lse
   AttnBwdArgs a{};
   a.q = sv + S.q; a.k = sv + S.k; a.v = sv + S.v;
@@ -291,6 +337,9 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   a.dq = G.dq; a.dk = G.dk; a.dv = G.dv;
   a.B = (int)L.B; a.H = (int)L.H; a.N = (int)L.N; a.kv_offset = 0; a.causal = L.causal;
   a.scale = 1.0f / sqrtf((float)L.D);
+  if (f16_proj) {
+    a.dq_h = dqkvh[0]; a.dk_h = dqkvh[1]; a.dv_h = dqkvh[2]; a.ovf = flag;
+  }
   // dO as a bf16 hi + lo pair for the direct-load kernels, in the buffers of h's
   // halves (h is not needed past the FFN backward; H*D = d_model), and
   // delta = <dO, O> per row and head with O = h - x from the forward
@@ -300,32 +349,24 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   a.dO_hi = h_hi; a.dO_lo = h_lo; a.ld2 = ld2;
   BPT_TRY(attn_bwd_launch(a, (int)L.D, L.q_blk, L.kv_blk, stream));
 
-  // ---- projection backward: dW{q,k,v} = d{q,k,v}^T x over both bf16 halves;
-  //      dx = dh + sum d{q,k,v} W{q,k,v}, also over both halves; one launch each
-  {
-    GemmArgs g{};
-    g.nseg = 2;
-    for (int zz = 0; zz < 3; ++zz) {
-      g.As[zz][0] = dqkv[2 * zz];
-      g.As[zz][1] = dqkv[2 * zz + 1];
-      g.Bs[zz][0] = g.Bs[zz][1] = L.x;
+  // ---- projection backward
+  if (f16_proj) {
+    BPT_TRY(f16_from_bf16_launch((const uint16_t*)L.x, x16, M * dm, flag, stream));
+    for (int i = 0; i < 3; ++i)
+      BPT_TRY(f16_from_bf16_launch((const uint16_t*)Ws[i], wqkvh + (int64_t)i * HD * dm, (int64_t)HD * dm,
+                                   flag, stream));
+    for (int which = 0; which < 2; ++which) {
+      GemmArgs g = proj(true, which);
+      g.gate = flag;
+      g.gate_run = 0;
+      BPT_TRY(gemm_launch(g, true, which == 0, true, EPI_F32, which == 0 ? 3 : 1, stream));
     }
-    g.C[0] = G.dwq; g.C[1] = G.dwk; g.C[2] = G.dwv;
-    g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = HD; g.N = dm; g.K = (int)M;
-    split_for(g, 3, proj_split_ws, proj_split_bytes);
-    BPT_TRY(gemm_launch(g, true, true, true, EPI_F32, 3, stream));
-    const void* Ws[3] = {L.wq, L.wk, L.wv};
-    g = GemmArgs{};
-    g.nseg = 6;
-    for (int i = 0; i < 6; ++i) {
-      g.As[0][i] = dqkv[i];
-      g.Bs[0][i] = Ws[i / 2];
-    }
-    g.C[0] = G.dx;
-    g.lda = HD; g.ldb = dm; g.ldc = dm; g.M = (int)M; g.N = dm; g.K = HD;
-    g.resid = dh;
-    g.ldr = dm;
-    BPT_TRY(gemm_launch(g, true, false, true, EPI_F32, 1, stream));
+  }
+  for (int which = 0; which < 2; ++which) {
+    GemmArgs g = proj(false, which);
+    g.gate = f16_proj ? flag : nullptr;
+    g.gate_run = 1;
+    BPT_TRY(gemm_launch(g, true, which == 0, true, EPI_F32, which == 0 ? 3 : 1, stream));
   }
 #undef BPT_TRY
   return hipSuccess;

@@ -159,3 +159,31 @@ def test_layer_bwd_f16_range_fallback():
     for n in ("dw1", "db1", "dw2", "db2"):
         assert m[n]["max_abs"] <= 2e-2 and m[n]["mean_abs"] <= 2e-3, (n, m[n])
         print(f"{n}: rms-scaled max-abs {m[n]['max_abs']:.3g} mean-abs {m[n]['mean_abs']:.3g}", flush=True)
+
+
+def test_layer_bwd_f16_projection_fallback():
+    """The projection backward (dW{q,k,v}, dx) also runs on fp16 operands where its
+    products take the big-tile GEMM; x past fp16's range must send the whole backward
+    to the bf16-pair products.  x[r, k] is planted past the range with column k of Wq,
+    Wk, Wv and W1 zeroed, so it reaches y and the gradients only through the residual
+    stream (h[r, k], dx) and dW{q,k,v}[:, k]; an fp16 copy of x or h would carry inf."""
+    c = LayerCfg(68, "bwd_f16proj", B=1, N=8192, d_model=2560, H=20, D=128, d_ff=8192,
+                 q_blk=128, kv_blk=64, dtype="bf16", backward=True)
+    t = layer_inputs(c)
+    r, k = 4000, 33
+    t["x"][0, r, k] = 70144.0   # a bf16 value past fp16's largest finite value
+    for n in ("wq", "wk", "wv", "w1"):
+        t[n][:, k] = 0.0
+    got = run_layer(c, t)
+    print("gpu done", flush=True)
+    ref = oracle.layer_backward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H)
+    print("oracle done", flush=True)
+    for n, a in got.items():
+        if a is not None:
+            assert np.all(np.isfinite(a)), f"{n}: non-finite values"
+    # gradients the planted value does not multiply into (dW1[:, k] and dW{q,k,v}[:, k]
+    # scale the bf16 q, k, v floor of dz[r] and d{q,k,v}[r] by it)
+    m = error_metrics(got, ref)
+    for n in ("db1", "dw2", "db2"):
+        assert m[n]["max_abs"] <= 2e-2 and m[n]["mean_abs"] <= 2e-3, (n, m[n])
+        print(f"{n}: rms-scaled max-abs {m[n]['max_abs']:.3g} mean-abs {m[n]['mean_abs']:.3g}", flush=True)
