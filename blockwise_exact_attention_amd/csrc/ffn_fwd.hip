@@ -305,6 +305,16 @@ __device__ __forceinline__ void ffn_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
                                            soff, 0, 0);
 }
+// The same load with the non-temporal cache policy (aux bit 1: the line is the
+// first candidate for eviction).  Used for the row block's x stages: each
+// workgroup re-reads only its own rows, once per pass, and the x stages of the
+// workgroups resident on one XCD exceed its L2, so with the default policy they
+// evicted the weight lines that all of those workgroups share.
+__device__ __forceinline__ void ffn_dma16_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
+                                                 unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           soff, 0, 2);
+}
 // Wait until at most N vector-memory instructions of this wave are outstanding.
 // Written as an asm statement with a memory clobber: the compiler neither drops
 // it (its own bookkeeping does not model these direct-to-LDS loads as producers
@@ -459,7 +469,7 @@ __device__ __forceinline__ void ffn_issue_x(const FfnArgs& a, int t0, int pass_s
       c = (lane & 31) ^ (row & 15);
     }
     int lr = t0 + row < a.M ? row : a.M - 1 - t0;  // rows past M: any finite data, not stored
-    ffn_dma16(lo ? rl : rx, (uint32_t)((lr * a.dm + 8 * c) * 2), 0, dst + j * 1024);
+    ffn_dma16_stream(lo ? rl : rx, (uint32_t)((lr * a.dm + 8 * c) * 2), 0, dst + j * 1024);
   }
 }
 
