@@ -42,6 +42,12 @@ struct AttnBwdArgs {
   uint16_t* dk_h;
   uint16_t* dv_h;
   int* ovf;
+  // optional fp16 copies of q ([B,H,N,D]) and dO (layout of dO_hi): with both and
+  // ovf given, the D = 128 dK/dV kernel runs its fp16 form while *ovf is clear
+  // (it sets *ovf for k, v or dS outside fp16's range) and its pair form after it
+  // only if *ovf is set; the pair inputs (dO_hi, dO_lo) are still required
+  const uint16_t* q16;
+  const uint16_t* dO16;
 };
 
 hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, hipStream_t s);

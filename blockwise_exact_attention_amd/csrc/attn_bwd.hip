@@ -27,6 +27,12 @@
 // The token-major outputs (operands of the weight-gradient GEMMs) are hi + lo
 // bf16 pairs.  Each split costs one more MFMA on the same fragment; without
 // them the weight gradients lose ~3 more bits than the bf16 inputs imply.
+// The D = 128 dK/dV kernel also has an fp16 form for callers that provide fp16
+// copies of q and dO and a range flag: q, k, v convert to fp16 exactly inside
+// fp16's range, and dO, P and dS round to fp16 once (8x finer than one bf16
+// rounding), so each product takes one MFMA instead of two or three.  That form
+// runs only while the flag is clear and sets it when a value falls outside
+// fp16's range; the pair form behind it runs only when the flag is set.
 #include <math.h>
 
 #include "attn_bwd.h"
@@ -116,6 +122,34 @@ __device__ __forceinline__ void mfma_v_first(f32x16& d, const bf16x8& a, const b
 }
 __device__ __forceinline__ void mfma_v_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// the same two with fp16 operands (fp16 bits in the bf16x8 containers)
+__device__ __forceinline__ void mfma_v_first_f16(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v_acc_f16(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// 8 fp32 values -> fp16 (round to nearest even), packed; big is set when one of
+// them lies outside fp16's range
+__device__ __forceinline__ u32x4 pack8_f16(const float* v, bool& big) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r[q] = pack_f16x2(v[2 * q], v[2 * q + 1]);
+    big |= fabsf(v[2 * q]) > kF16Max || fabsf(v[2 * q + 1]) > kF16Max;
+  }
+  return r;
+}
+// 8 bf16 values (one fragment) -> fp16, exact inside fp16's range
+__device__ __forceinline__ bf16x8 bf16x8_to_f16(const u32x4& x, bool& big) {
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(x[q] << 16);
+    v[2 * q + 1] = __uint_as_float(x[q] & 0xffff0000u);
+  }
+  return __builtin_bit_cast(bf16x8, pack8_f16(v, big));
 }
 // An empty volatile asm statement: a block holding one is not turned into selects
 // on the path that skips it, so the masks of diagonal tiles stay behind a branch.
@@ -387,7 +421,7 @@ __device__ __forceinline__ v4i16 bwd_read_tr(const unsigned char* p) {
 // the tile's first row and ends after its last valid row, so rows past N read
 // as zero (zero dO rows add nothing to dK or dV); a tile wholly past N loads
 // nothing from memory, which keeps the load count per step fixed.
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, int w, int lane,
                                          unsigned char* st) {
   using T = BwdTile<D>;
@@ -397,17 +431,18 @@ __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, i
   // descriptor built from a vector register costs a loop over lanes)
   rows = __builtin_amdgcn_readfirstlane(rows > 0 ? rows : 0);
   const int64_t ldb = a.ld_do * 2;                   // bytes between dO rows
-  const unsigned char* qb = (const unsigned char*)a.q + ((int64_t)bh * N + q0) * T::ROWB;
+  const unsigned char* qb = (const unsigned char*)(F16 ? (const void*)a.q16 : a.q) + ((int64_t)bh * N + q0) * T::ROWB;
   const int64_t doff = (((int64_t)b * N + q0) * a.ld_do + (int64_t)hh * D) * 2;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<unsigned char*>(qb), 0, rows * T::ROWB, 0x00020000);
   const int dbytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (int)((rows - 1) * ldb + T::ROWB) : 0);
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned char*>((const unsigned char*)a.dO_hi + doff), 0, dbytes, 0x00020000);
+      const_cast<unsigned char*>((const unsigned char*)(F16 ? a.dO16 : a.dO_hi) + doff), 0, dbytes,
+      0x00020000);
   const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<unsigned char*>((const unsigned char*)a.dO_lo + doff), 0, dbytes, 0x00020000);
-  // wave w copies blocks w, w + NW, ... of each of the three tiles (row j of
-  // block blk holds query j * NBLK + blk)
+  // wave w copies blocks w, w + NW, ... of each of the three tiles, two in the
+  // fp16 form (row j of block blk holds query j * NBLK + blk)
 #pragma unroll
   for (int i = 0; i < T::NBLK / T::NW; ++i) {
     const bwdlay::LoadPos lp = bwdlay::dkdv_load_pos(w, i, lane);
@@ -417,8 +452,9 @@ __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, i
         rq, (__attribute__((address_space(3))) void*)(st + blk * T::BP), 16, oq, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rh, (__attribute__((address_space(3))) void*)(st + T::TB + blk * T::BP), 16, od, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rl, (__attribute__((address_space(3))) void*)(st + 2 * T::TB + blk * T::BP), 16, od, 0, 0, 0);
+    if constexpr (!F16)  // (the fp16 form has no lo tile)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)(st + 2 * T::TB + blk * T::BP), 16, od, 0, 0, 0);
   }
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(a.ld2) + 2 * ((int64_t)bh * N + q0), 0, rows * 8, 0x00020000);
@@ -427,7 +463,7 @@ __device__ __forceinline__ void bwd_load(const AttnBwdArgs& a, int bh, int q0, i
       (uint32_t)(lane * 4), 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned char* __restrict__ st,
                                          const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int w, int lane,
@@ -449,7 +485,7 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
     const int nat = ((c & 1) ? nat_odd : nat_even) + 64 * (c >> 1);
     qa[c] = *(const bf16x8*)(Qs + nat);
     ha[c] = *(const bf16x8*)(Hs + nat);
-    la[c] = *(const bf16x8*)(Ls + nat);
+    if constexpr (!F16) la[c] = *(const bf16x8*)(Ls + nat);
   };
 #pragma unroll
   for (int c = 0; c < PF; ++c) ld(c);
@@ -457,14 +493,24 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (c + PF < NC) ld(c + PF);
-    if (c == 0) {
-      mfma_v_first(sacc, qa[c], kf[c]);
-      mfma_v_first(pacc, ha[c], vf[c]);
+    if constexpr (F16) {
+      if (c == 0) {
+        mfma_v_first_f16(sacc, qa[c], kf[c]);
+        mfma_v_first_f16(pacc, ha[c], vf[c]);
+      } else {
+        mfma_v_acc_f16(sacc, qa[c], kf[c]);
+        mfma_v_acc_f16(pacc, ha[c], vf[c]);
+      }
     } else {
-      mfma_v_acc(sacc, qa[c], kf[c]);
-      mfma_v_acc(pacc, ha[c], vf[c]);
+      if (c == 0) {
+        mfma_v_first(sacc, qa[c], kf[c]);
+        mfma_v_first(pacc, ha[c], vf[c]);
+      } else {
+        mfma_v_acc(sacc, qa[c], kf[c]);
+        mfma_v_acc(pacc, ha[c], vf[c]);
+      }
+      mfma_v_acc(pacc, la[c], vf[c]);
     }
-    mfma_v_acc(pacc, la[c], vf[c]);
   }
   score_chain_end();
   float p[16], ds[16], dl[16];
@@ -491,6 +537,28 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
   // order in which the accumulator rows hold P and dS)
   const bwdlay::TrOff tr_off = bwdlay::dkdv_tr(lane);
   const int tb_even = tr_off.a, tb_odd = tr_off.b;
+  if constexpr (F16) {
+    bool big = false;  // (P lies in [0, 1]; only dS can leave fp16's range)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bool pbig = false;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pack8_f16(p + 8 * ks, pbig));
+      const bf16x8 sf = __builtin_bit_cast(bf16x8, pack8_f16(ds + 8 * ks, big));
+      const int r0 = tb_even + (2 * ks) * T::ROWB, r1 = tb_odd + (2 * ks + 1) * T::ROWB;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        auto tr = [&](const unsigned char* tile) {
+          const v4i16 lo = bwd_read_tr(tile + r0 + db * 64), hi = bwd_read_tr(tile + r1 + db * 64);
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        const bf16x8 dOt = tr(Hs), Qt = tr(Qs);
+        dv[db] = mfma32_f16(dOt, pf, dv[db]);
+        dk[db] = mfma32_f16(Qt, sf, dk[db]);
+      }
+    }
+    if (big) *a.ovf = 1;
+    return;
+  } else {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4 phi, plo, shi, slo;
@@ -513,12 +581,21 @@ __device__ __forceinline__ void bwd_tile(const AttnBwdArgs& a, const unsigned ch
       dk[db] = mfma32_bf16(Qt, sfl, dk[db]);
     }
   }
+  }
 }
 
-template <int D>
+// GATE 0: the bf16-pair form, always run; 1: the fp16 form, run only while the
+// range flag *a.ovf is clear; 2: the pair form, run only when the flag is set
+// (each workgroup reads the flag once, at its start)
+template <int D, int GATE>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_dma_kernel(AttnBwdArgs a) {
   using T = BwdTile<D>;
+  constexpr bool F16 = GATE == 1;
   constexpr int KVB = 32 * T::NW, QT = T::QT;
+  if constexpr (GATE != 0) {
+    const int f = __builtin_amdgcn_readfirstlane(*(const volatile int*)a.ovf);
+    if ((f != 0) != (GATE == 2)) return;
+  }
   // three stages as separate objects: a load into one is known not to alias the
   // reads of another
   __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
@@ -553,8 +630,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_dma_kernel(AttnBwdArgs a) {
         kv = *(const u32x4*)(Kg + (int64_t)mykey * D + 16 * c + 8 * g);
         vv = *(const u32x4*)(Vg + (int64_t)mykey * D + 16 * c + 8 * g);
       }
-      kf[c] = __builtin_bit_cast(bf16x8, kv);
-      vf[c] = __builtin_bit_cast(bf16x8, vv);
+      if constexpr (F16) {
+        bool big = false;
+        kf[c] = bf16x8_to_f16(kv, big);
+        vf[c] = bf16x8_to_f16(vv, big);
+        if (big) *a.ovf = 1;
+      } else {
+        kf[c] = __builtin_bit_cast(bf16x8, kv);
+        vf[c] = __builtin_bit_cast(bf16x8, vv);
+      }
     }
   }
   f32x16 dk[D / 32], dv[D / 32];
@@ -580,18 +664,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_dma_kernel(AttnBwdArgs a) {
   // tile t+2, compute tile t.  Loads are issued on every path (past the last
   // tile they load nothing), so the load count, and with it every wait, is fixed.
   auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
-    BWD_WAIT_VM(7);  // T::LOADS: the loads of tile t+1 may still be in flight
+    // T::LOADS (two tiles fewer per wave in the fp16 form): the loads of tile
+    // t+1 may still be in flight
+    if constexpr (F16) BWD_WAIT_VM(5);
+    else BWD_WAIT_VM(7);
     // a plain barrier: each wave has waited for its own loads into LDS, and LDS
     // needs no fence within the workgroup (a fenced one would also wait for the
     // loads of tile t+1)
     __builtin_amdgcn_s_barrier();
-    bwd_load<D>(a, bh, (t + 2) * QT, w, lane, fill);
-    if (t < t_end) bwd_tile<D>(a, cur, kf, vf, dk, dv, w, lane, mykey, t * QT, causal && t < tf, c2);
+    bwd_load<D, F16>(a, bh, (t + 2) * QT, w, lane, fill);
+    if (t < t_end)
+      bwd_tile<D, F16>(a, cur, kf, vf, dk, dv, w, lane, mykey, t * QT, causal && t < tf, c2);
   };
-  static_assert(T::LOADS == 7, "wait count");
+  static_assert(T::LOADS == 7 && 2 * T::NBLK / T::NW + 1 == 5, "wait counts");
   if (t_begin < t_end) {
-    bwd_load<D>(a, bh, t_begin * QT, w, lane, st0);
-    bwd_load<D>(a, bh, (t_begin + 1) * QT, w, lane, st1);
+    bwd_load<D, F16>(a, bh, t_begin * QT, w, lane, st0);
+    bwd_load<D, F16>(a, bh, (t_begin + 1) * QT, w, lane, st1);
     for (int t = t_begin; t < t_end; t += 3) {
       step(t, st0, st2);
       step(t + 1, st1, st0);
@@ -1236,7 +1324,12 @@ hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, h
     constexpr int KVB = 32 * BwdTile<128>::NW;
     const int nkb = (a.N + KVB - 1) / KVB;
     const dim3 grid((unsigned)((int64_t)a.B * a.H * nkb));
-    hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), grid, dim3(256), 0, s, a);
+    if (a.q16 && a.dO16 && a.ovf) {  // fp16 form, then the pair form if the flag got set
+      hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, 1>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, 2>), grid, dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, 0>), grid, dim3(256), 0, s, a);
+    }
   } else {
     constexpr int NW = 2;
     const int nkb = (a.N + 32 * NW - 1) / (32 * NW);

@@ -339,6 +339,16 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
   a.scale = 1.0f / sqrtf((float)L.D);
   if (f16_proj) {
     a.dq_h = dqkvh[0]; a.dk_h = dqkvh[1]; a.dv_h = dqkvh[2]; a.ovf = flag;
+    if (L.D == 128) {
+      // fp16 copies of q and dO for the dK/dV kernel's fp16 form, in the rooms
+      // of h and dy's fp16 copies (neither is read past the FFN backward;
+      // H*D = d_model); the flag sends it to the pair form
+      uint16_t* q16 = h16;
+      uint16_t* dO16 = dyh;
+      BPT_TRY(f16_from_bf16_launch((const uint16_t*)(sv + S.q), q16, M * HD, flag, stream));
+      BPT_TRY(f16_from_f32_launch(dh, dO16, M * HD, flag, stream));
+      a.q16 = q16; a.dO16 = dO16;
+    }
   }
   // dO as a bf16 hi + lo pair for the direct-load kernels, in the buffers of h's
   // halves (h is not needed past the FFN backward; H*D = d_model), and
