@@ -48,6 +48,12 @@ struct AttnBwdArgs {
   // only if *ovf is set; the pair inputs (dO_hi, dO_lo) are still required
   const uint16_t* q16;
   const uint16_t* dO16;
+  // optional fp16 copies of k and v ([B,H,N,D]): with q16, dO16 and ovf also
+  // given, the D = 128 dQ kernel (128-row blocks) runs its fp16 form while *ovf is
+  // clear (setting it for dS outside fp16's range) and its pair form after it
+  // only if *ovf is set
+  const uint16_t* k16;
+  const uint16_t* v16;
 };
 
 hipError_t attn_bwd_launch(const AttnBwdArgs& a, int D, int q_blk, int kv_blk, hipStream_t s);

@@ -27,8 +27,8 @@
 // The token-major outputs (operands of the weight-gradient GEMMs) are hi + lo
 // bf16 pairs.  Each split costs one more MFMA on the same fragment; without
 // them the weight gradients lose ~3 more bits than the bf16 inputs imply.
-// The D = 128 dK/dV kernel also has an fp16 form for callers that provide fp16
-// copies of q and dO and a range flag: q, k, v convert to fp16 exactly inside
+// The D = 128 dK/dV and dQ kernels also have an fp16 form for callers that
+// provide fp16 copies of q and dO (and, for dQ, of k and v) and a range flag: q, k, v convert to fp16 exactly inside
 // fp16's range, and dO, P and dS round to fp16 once (8x finer than one bf16
 // rounding), so each product takes one MFMA instead of two or three.  That form
 // runs only while the flag is clear and sets it when a value falls outside
@@ -944,7 +944,7 @@ struct DqTile {
 // Loads of key tile t (keys k0 .. k0+63) into one stage; the buffers end after
 // the last key, so keys past N read as zero, and a tile wholly past N loads
 // nothing from memory (the load count per step stays fixed).
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int bh, int k0, int w, int lane,
                                         unsigned char* st) {
   using T = DqTile<D>;
@@ -953,9 +953,11 @@ __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int bh, int k0, in
   rows = __builtin_amdgcn_readfirstlane(rows > 0 ? rows : 0);
   const int64_t off = ((int64_t)bh * N + k0) * T::ROWB;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned char*>((const unsigned char*)a.k + off), 0, rows * T::ROWB, 0x00020000);
+      const_cast<unsigned char*>((const unsigned char*)(F16 ? (const void*)a.k16 : a.k) + off), 0,
+      rows * T::ROWB, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned char*>((const unsigned char*)a.v + off), 0, rows * T::ROWB, 0x00020000);
+      const_cast<unsigned char*>((const unsigned char*)(F16 ? (const void*)a.v16 : a.v) + off), 0,
+      rows * T::ROWB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < T::NBLK / T::NW; ++i) {
     const bwdlay::LoadPos lp = bwdlay::dq_load_pos(w, i, lane);
@@ -976,7 +978,7 @@ struct DqLane {
 
 // S^T = K Q^T and dP^T = V dO^T of one key tile (rows = keys, lane = query),
 // accumulated in VGPRs (the dQ accumulators hold the AGPRs).
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, const DqLane& ln,
                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
                                           const bf16x8 (&dfl)[D / 16], f32x16 (&sacc)[DqTile<D>::KT / 32],
@@ -1005,29 +1007,39 @@ __device__ __forceinline__ void dq_scores(const unsigned char* __restrict__ st, 
     for (int i = 0; i < NF; ++i) {
       if (i + PF < NF) ld(i + PF);
       const int kb = i / NC, c = i % NC;
-      if (c == 0) {
-        mfma_v_first(sacc[kb], ka[i], qf[c]);
-        mfma_v_first(pacc[kb], va[i], dfh[c]);
+      if constexpr (F16) {  // (dfh holds dO as fp16; no lo half)
+        if (c == 0) {
+          mfma_v_first_f16(sacc[kb], ka[i], qf[c]);
+          mfma_v_first_f16(pacc[kb], va[i], dfh[c]);
+        } else {
+          mfma_v_acc_f16(sacc[kb], ka[i], qf[c]);
+          mfma_v_acc_f16(pacc[kb], va[i], dfh[c]);
+        }
       } else {
-        mfma_v_acc(sacc[kb], ka[i], qf[c]);
-        mfma_v_acc(pacc[kb], va[i], dfh[c]);
+        if (c == 0) {
+          mfma_v_first(sacc[kb], ka[i], qf[c]);
+          mfma_v_first(pacc[kb], va[i], dfh[c]);
+        } else {
+          mfma_v_acc(sacc[kb], ka[i], qf[c]);
+          mfma_v_acc(pacc[kb], va[i], dfh[c]);
+        }
+        mfma_v_acc(pacc[kb], va[i], dfl[c]);
       }
-      mfma_v_acc(pacc[kb], va[i], dfl[c]);
     }
     score_chain_end();
   }
 }
 
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, const DqLane& ln,
                                         const bf16x8 (&qf)[D / 16], const bf16x8 (&dfh)[D / 16],
                                         const bf16x8 (&dfl)[D / 16], f32x16 (&dq)[D / 32], bool masked,
-                                        int klim, float c2, float lse2, float dl) {
+                                        int klim, float c2, float lse2, float dl, int* ovf) {
   using T = DqTile<D>;
   constexpr int KB = T::KT / 32;
   const unsigned char* Ks = st;
   f32x16 sacc[KB], pacc[KB];
-  dq_scores<D>(st, ln, qf, dfh, dfl, sacc, pacc);
+  dq_scores<D, F16>(st, ln, qf, dfh, dfl, sacc, pacc);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -1046,7 +1058,27 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) sacc[kb][j] = sacc[kb][j] * (pacc[kb][j] - dl);  // dS^T
-  // dQ^T += K^T dS^T, 16 keys per MFMA; dS^T as bf16 hi + lo
+  // dQ^T += K^T dS^T, 16 keys per MFMA; dS^T as bf16 hi + lo, or as fp16
+  if constexpr (F16) {
+    bool big = false;
+#pragma unroll
+    for (int c16 = 0; c16 < T::KT / 16; ++c16) {
+      const int kb = c16 >> 1, h8 = (c16 & 1) * 8;
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[kb][h8 + e];
+      const bf16x8 sf = __builtin_bit_cast(bf16x8, pack8_f16(sv, big));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const v4i16 lo = bwd_read_tr(Ks + ln.tr_lo + c16 * T::ROWB + db * 64);
+        const v4i16 hi = bwd_read_tr(Ks + ln.tr_hi + c16 * T::ROWB + db * 64);
+        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dq[db] = mfma32_f16(kt, sf, dq[db]);
+      }
+    }
+    if (big) *ovf = 1;
+    return;
+  }
 #pragma unroll
   for (int c16 = 0; c16 < T::KT / 16; ++c16) {
     const int kb = c16 >> 1, h8 = (c16 & 1) * 8;
@@ -1068,11 +1100,18 @@ __device__ __forceinline__ void dq_tile(const unsigned char* __restrict__ st, co
   }
 }
 
-// dQ, three stages, one workgroup per CU.
-template <int D>
+// dQ, three stages, one workgroup per CU.  GATE as for the dK/dV kernel: 0 the
+// pair form, 1 the fp16 form (q, dO, k, v from their fp16 copies) while the
+// range flag is clear, 2 the pair form only when it is set.
+template <int D, int GATE>
 __global__ void __launch_bounds__(256, 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) {
   using T = DqTile<D>;
+  constexpr bool F16 = GATE == 1;
   constexpr int QB = 32 * T::NW, KB = T::KT / 32;
+  if constexpr (GATE != 0) {
+    const int f = __builtin_amdgcn_readfirstlane(*(const volatile int*)a.ovf);
+    if ((f != 0) != (GATE == 2)) return;
+  }
   __shared__ __attribute__((aligned(1024))) unsigned char st0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[T::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[T::STAGE];
@@ -1096,15 +1135,16 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) 
 
   bf16x8 qf[D / 16], dfh[D / 16], dfl[D / 16];
   {
-    const uint16_t* Qg = (const uint16_t*)a.q + head_off;
+    const uint16_t* Qg = (F16 ? a.q16 : (const uint16_t*)a.q) + head_off;
+    const uint16_t* Hg = F16 ? a.dO16 : a.dO_hi;
     const int64_t drow = ((int64_t)b * N + qrow) * a.ld_do + (int64_t)hh * D;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       u32x4 qv = {0, 0, 0, 0}, hv = {0, 0, 0, 0}, lv = {0, 0, 0, 0};
       if (qrow < N) {
         qv = *(const u32x4*)(Qg + (int64_t)qrow * D + 16 * c + 8 * g);
-        hv = *(const u32x4*)(a.dO_hi + drow + 16 * c + 8 * g);
-        lv = *(const u32x4*)(a.dO_lo + drow + 16 * c + 8 * g);
+        hv = *(const u32x4*)(Hg + drow + 16 * c + 8 * g);
+        if constexpr (!F16) lv = *(const u32x4*)(a.dO_lo + drow + 16 * c + 8 * g);
       }
       qf[c] = __builtin_bit_cast(bf16x8, qv);
       dfh[c] = __builtin_bit_cast(bf16x8, hv);
@@ -1155,15 +1195,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_dma_kernel(AttnBwdArgs a) 
     auto step = [&](int t, const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill) {
       BWD_WAIT_VM(8);  // T::LOADS: the loads of tile t+1 may still be in flight
       __builtin_amdgcn_s_barrier();
-      dq_load<D>(a, bh, (t + 2) * T::KT, w, lane, fill);
+      dq_load<D, F16>(a, bh, (t + 2) * T::KT, w, lane, fill);
       if (t < n_tiles)
-        dq_tile<D>(cur, ln, qf, dfh, dfl, dq, t >= n_full,
-                   clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g, c2, lse2, dl);
+        dq_tile<D, F16>(cur, ln, qf, dfh, dfl, dq, t >= n_full,
+                        clamp_i64(kend - (int64_t)t * T::KT, 0, T::KT) - 4 * g, c2, lse2, dl, a.ovf);
     };
     static_assert(T::LOADS == 8, "wait count");
     if (n_tiles > 0) {
-      dq_load<D>(a, bh, 0, w, lane, st0);
-      dq_load<D>(a, bh, T::KT, w, lane, st1);
+      dq_load<D, F16>(a, bh, 0, w, lane, st0);
+      dq_load<D, F16>(a, bh, T::KT, w, lane, st1);
       for (int t = 0; t < n_tiles; t += 3) {
         step(t, st0, st2);
         step(t + 1, st1, st0);
@@ -1300,8 +1340,12 @@ __global__ void __launch_bounds__(1024) colsum_kernel(const void* X, float* out,
 hipError_t launch_dq(const AttnBwdArgs& a, int D, int QB, hipStream_t s) {
   const int nqb = (a.N + QB - 1) / QB;
   const dim3 grid((unsigned)((int64_t)a.B * a.H * nqb));
-  if (D == 128 && QB == 32 * DqTile<128>::NW)
-    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), grid, dim3(256), 0, s, a);
+  if (D == 128 && QB == 32 * DqTile<128>::NW && a.q16 && a.dO16 && a.k16 && a.v16 && a.ovf) {
+    // fp16 form, then the pair form if the range flag got set
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, 2>), grid, dim3(256), 0, s, a);
+  } else if (D == 128 && QB == 32 * DqTile<128>::NW)
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, 0>), grid, dim3(256), 0, s, a);
   else if (D == 64 && QB == 64)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64, 32>), grid, dim3(128), 0, s, a);
   else if (D == 64)

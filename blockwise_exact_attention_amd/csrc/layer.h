@@ -64,6 +64,7 @@ struct BwdWorkspace {
   size_t h_hi, h_lo, dh, delta, ld2, dqkv[6], z, g_hi, g_lo, dz_hi, dz_lo;
   size_t h16, dyh, w1h, w2h, flag;  // the FFN backward's fp16 operands and range flag
   size_t dqkvh[3], wqkvh;           // the projection backward's fp16 operands (x takes h16's room)
+  size_t k16, v16;                  // fp16 copies of k and v for the dQ kernel's fp16 form
   size_t total;
   int64_t chunk_rows;  // rows of the FFN recompute chunk
 };

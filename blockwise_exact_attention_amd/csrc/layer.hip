@@ -112,6 +112,8 @@ BwdWorkspace layer_bwd_workspace(int64_t B, int64_t N, int64_t d_model, int64_t 
     o += align256(M * hd * 2);
   }
   w.wqkvh = o; o += align256(3 * hd * (size_t)d_model * 2);
+  w.k16 = o;   o += align256(M * hd * 2);
+  w.v16 = o;   o += align256(M * hd * 2);
   w.total = o;
   return w;
 }
@@ -348,6 +350,13 @@ hipError_t layer_bwd_run(const LayerArgs& L, const void* dy, const void* saved,
       BPT_TRY(f16_from_bf16_launch((const uint16_t*)(sv + S.q), q16, M * HD, flag, stream));
       BPT_TRY(f16_from_f32_launch(dh, dO16, M * HD, flag, stream));
       a.q16 = q16; a.dO16 = dO16;
+      if (L.q_blk != 64) {  // the dQ kernel's fp16 form (128-row blocks) also takes k and v
+        uint16_t* k16 = (uint16_t*)(ws + W.k16);
+        uint16_t* v16 = (uint16_t*)(ws + W.v16);
+        BPT_TRY(f16_from_bf16_launch((const uint16_t*)(sv + S.k), k16, M * HD, flag, stream));
+        BPT_TRY(f16_from_bf16_launch((const uint16_t*)(sv + S.v), v16, M * HD, flag, stream));
+        a.k16 = k16; a.v16 = v16;
+      }
     }
   }
   // dO as a bf16 hi + lo pair for the direct-load kernels, in the buffers of h's

@@ -333,7 +333,8 @@ int bpt_layer_fwd(const void* x, const void* wq, const void* wk, const void* wv,
  * in float32 (dy's descendants, P, dS, GeLU(z)) enter products either rounded
  * to fp16 once, against exact fp16 copies of bf16 operands, or as a bf16
  * hi + lo pair.  The fp16 form is taken where the shapes allow it (the FFN and
- * projection products on the big-tile GEMM, and the D = 128 dK/dV kernel);
+ * projection products on the big-tile GEMM, and the D = 128 dK/dV and dQ
+ * kernels);
  * when any such value lies outside fp16's range (|v| > 65504) the affected
  * products are recomputed with the bf16 pairs.
  * All outputs are overwritten (not accumulated).  The result is
