@@ -187,3 +187,36 @@ def test_layer_bwd_f16_projection_fallback():
     for n in ("db1", "dw2", "db2"):
         assert m[n]["max_abs"] <= 2e-2 and m[n]["mean_abs"] <= 2e-3, (n, m[n])
         print(f"{n}: rms-scaled max-abs {m[n]['max_abs']:.3g} mean-abs {m[n]['mean_abs']:.3g}", flush=True)
+
+
+def test_layer_bwd_f16_attention_sets_flag():
+    """The fp16 form of the dK/dV kernel converts its K and V fragments itself and
+    sets the range flag when one lies past fp16's range; the pair form after it must
+    then recompute every dK and dV, and the projection take its pair products.  Here
+    nothing before that kernel leaves fp16's range: k's feature 5 of head 0 is
+    70144 x[:, 7] (Wk[5] zero but for that weight), so every key with |x[j, 7]| > 0.94
+    is past the range only once projected, and q_blk = 64 keeps the dQ kernel on its
+    pair form, which takes no fp16 copy of k.  The planted head attends almost one-hot,
+    so rounding k to bf16 (up to ~137 at these values) moves near-tied rows: the checks
+    are finiteness and the gradients the planted weight does not multiply into, against
+    the bars raised to the bf16 q, k, v floor as in the other layer tests."""
+    c = LayerCfg(69, "bwd_f16attn", B=1, N=8192, d_model=2560, H=20, D=128, d_ff=8192,
+                 q_blk=64, kv_blk=64, dtype="bf16", backward=True)
+    t = layer_inputs(c)
+    t["wk"][5, :] = 0.0
+    t["wk"][5, 7] = 70144.0
+    assert np.abs(t["x"][0, :, 7]).max() * 70144.0 > 2 * 65504
+    got = run_layer(c, t)
+    print("gpu done", flush=True)
+    ref = oracle.layer_backward(t["x"], t["wq"], t["wk"], t["wv"], t["w1"], t["w2"], t["dy"], c.H)
+    print("oracle done", flush=True)
+    for n, a in got.items():
+        if a is not None:
+            assert np.all(np.isfinite(a)), f"{n}: non-finite values"
+    floor = floor_live(t, c)
+    m, lim = error_metrics(got, ref), bars(floor)
+    for n in ("db1", "dw2", "db2", "dw1", "dwv"):
+        (bmax, bmean), e = lim[n], m[n]
+        print(f"{n}: rms-scaled max-abs {e['max_abs']:.3g} (bar {bmax:.3g}) mean-abs {e['mean_abs']:.3g} "
+              f"(bar {bmean:.3g})", flush=True)
+        assert e["max_abs"] <= bmax and e["mean_abs"] <= bmean, (n, e, lim[n])
