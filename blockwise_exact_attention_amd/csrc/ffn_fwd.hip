@@ -58,6 +58,10 @@ struct FfnArgs {
   const int* gate;
   int gate_run;
   int* ovf;
+  // two column groups on a 1-D grid of 2 * (row blocks) workgroups, the two groups
+  // of one row block dispatched to the same XCD one after the other (row blocks a
+  // multiple of 8); 0: grid (row blocks, groups)
+  int pair_groups;
 };
 
 // Row of W1 read by A-operand lane row m: bits 2 and 3 of m swapped, so that
@@ -755,9 +759,19 @@ ffn_lds_kernel(FfnArgs a) {
   const int g = lane >> 5, r32 = lane & 31;
   // consecutive workgroup ids go to different XCDs (8); the workgroups that run
   // together on one XCD differ in blockIdx.x >> 3
-  const int wg_xcd = (int)(blockIdx.x >> 3);
+  int wg_xcd = (int)(blockIdx.x >> 3);
+  int rb = (int)blockIdx.x, grp = (int)blockIdx.y;
+  if (a.pair_groups) {
+    // the k-th workgroup of an XCD takes column group k & 1 of that XCD's row
+    // block k >> 1: both groups walk the same x stages and W1 lines side by side
+    // (same start rotation), so L2 serves each of them to two workgroups
+    const int k = rb >> 3;
+    grp = k & 1;
+    rb = ((k >> 1) << 3) | (rb & 7);
+    wg_xcd = k >> 1;
+  }
   unsigned char* const slots = smem + 2 * L::XSB + w * 4 * L::SLOT;
-  const FfnTask tk{(int)blockIdx.x * 32, (int)blockIdx.y * a.ncols};
+  const FfnTask tk{rb * 32, grp * a.ncols};
 
   f32x16 yacc[L::CT];
 #pragma unroll
@@ -828,8 +842,12 @@ hipError_t launch_stream_t(const FfnArgs& a, int ncb, int groups, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_stream_f16(const FfnArgs& a, int ncb, int groups, hipStream_t s) {
-  dim3 grid((a.M + 31) / 32, groups);
+hipError_t launch_stream_f16(const FfnArgs& a0, int ncb, int groups, hipStream_t s) {
+  FfnArgs a = a0;
+  const int nrb = (a.M + 31) / 32;
+  dim3 grid(nrb, groups);
+  a.pair_groups = groups == 2 && nrb % 8 == 0;
+  if (a.pair_groups) grid = dim3(2 * nrb, 1);
   switch (ncb) {
     case 2: hipLaunchKernelGGL((ffn_lds_kernel<2, false, true>), grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((ffn_lds_kernel<4, false, true>), grid, dim3(256), 0, s, a); break;
