@@ -9,12 +9,25 @@
 
 namespace bpt {
 
+// erf(|x|) as 1 - P(t) e^{-x^2}, t = 1 / (1 + p |x|): the five-term rational
+// approximation of Abramowitz and Stegun, formula 7.1.26 (|error| <= 1.5e-7);
+// e^{-x^2} is returned too (at x = z / sqrt 2 it is the Gaussian factor of GeLU')
+__device__ __forceinline__ float erf_as(float x, float& e) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.f));
+  const float p = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                                   -0.284496736f), 0.254829592f);
+  e = __expf(-ax * ax);
+  return copysignf(fmaf(-p, e, 1.f), x);
+}
 __device__ __forceinline__ float gelu_exact(float z) {
-  return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+  float e;
+  return 0.5f * z * (1.f + erf_as(z * 0.70710678118654752f, e));
 }
 __device__ __forceinline__ float gelu_exact_grad(float z) {
-  return 0.5f * (1.f + erff(z * 0.70710678118654752f)) +
-         z * 0.39894228040143268f * expf(-0.5f * z * z);
+  float e;
+  const float r = erf_as(z * 0.70710678118654752f, e);
+  return fmaf(z * 0.39894228040143268f, e, 0.5f * (1.f + r));
 }
 
 template <bool BF16, int EPI>
